@@ -1,0 +1,12 @@
+"""MI355X-native fused GEMM + ReLU: C = ReLU(A @ B) on gfx950 MFMA."""
+from .binding import (  # noqa: F401
+    gemm_relu,
+    gemm_relu_raw,
+    selected_config,
+    strerror,
+    library_path,
+    load_library,
+    GemmReluError,
+    F16,
+    BF16,
+)
