@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of C = ReLU(A @ B) on one MI355X.
+
+One step is one call of the library's gemm_relu (every step of the path: tile
+loads, MFMA contraction, ReLU, cast, store) on one batch of synthetic input
+already resident in HBM.  The default workload is the 8192^3 fp16 GEMM with
+inputs N(0, 1) * 0.1; three separately allocated input/output sets are rotated
+so that repeated reads are not served from the 256 MB MALL.
+
+Timing follows the method of "TileLang Guide: Composable Tiled AI Kernel
+Programming" (Step 2, the benchmark script): warm-up calls, then timed calls
+between GPU events, throughput = 2*M*N*K / t.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import tiled_dense_gemm_relu_amd as gr  # noqa: E402
+from tiled_dense_gemm_relu_amd import binding, inputs  # noqa: E402
+
+PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}     # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0                               # MI355X HBM3E, published
+METRIC = "TFLOP/s and % of MI355X dense fp16 MFMA peak, ReLU(A@B) 8192³"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_sets(w, n_sets, device):
+    sets = []
+    for i in range(n_sets):
+        g_seed = w.seed + 1000 * i
+        a, b = inputs.normal_pair(w.M, w.N, w.K, w.torch_dtype, w.scale, g_seed)
+        c = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=device)
+        sets.append((a.to(device), b.to(device), c))
+    return sets
+
+
+def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO):
+    """Returns (ms per step over the timed region, mean kernel ms from per-launch events)."""
+    sets = make_sets(w, n_sets, device)
+    stream = torch.cuda.current_stream(device)
+    dt = binding.F16 if w.dtype == "fp16" else binding.BF16
+
+    def launch(i):
+        a, b, c = sets[i % n_sets]
+        rc = binding.gemm_relu_raw(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, dt,
+                                   stream.cuda_stream, config)
+        if rc != 0:
+            raise binding.GemmReluError(rc, gr.strerror(rc))
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize(device)
+
+    # Timed region: K steps between two events; each launch is also bracketed by
+    # its own pair of events on the same stream, for the kernel's mean duration.
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize(device)
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize(device)
+    total_ms = t0.elapsed_time(t1)
+    kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    del sets
+    return total_ms / steps, kernel_ms
+
+
+def cpu_baseline(w, target_s):
+    """The CPU oracle on a bounded sample of the workload: whole rows of C."""
+    import oracle
+    a, b = inputs.workload_inputs(w)
+    threads = len(os.sched_getaffinity(0))
+    # Grow the row count until one run takes at least half the target time
+    # (the first runs are short; only the last, longest run is reported).
+    rows = max(1, threads)
+    while True:
+        t = time.perf_counter()
+        oracle.gemm_relu_rows(a, b, w.dtype, 0, rows, threads=threads)
+        dt = time.perf_counter() - t
+        if dt >= 0.5 * target_s or rows >= w.M:
+            break
+        rows = int(min(w.M, max(rows + 1, rows * target_s / max(dt, 1e-3))))
+    rows_target = rows
+    flop = 2.0 * rows_target * w.N * w.K
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows_target - 1} of C ({rows_target} x {w.N} x {w.K}), "
+                      f"{dt:.1f} s wall, fp64 accumulation",
+            "seconds": dt}
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="square_8192", choices=sorted(inputs.WORKLOADS))
+    p.add_argument("--sets", type=int, default=3, help="rotated input/output sets")
+    p.add_argument("--config", type=int, default=binding.CONFIG_AUTO)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
+    args = p.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    gr.load_library()
+
+    w = inputs.WORKLOADS[args.workload]
+    cfg = gr.selected_config(w.M, w.N, w.K, binding.F16 if w.dtype == "fp16" else binding.BF16, args.config)
+    log(f"[bench] {w.name}: config {cfg}")
+    ms_step, kernel_ms = time_workload(w, args.steps, args.warmup, args.sets, device, args.config)
+    tflops = w.flop / (ms_step * 1e-3) / 1e12
+    kernel_tflops = w.flop / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"[bench] {w.name}: {ms_step:.4f} ms/step, {tflops:.1f} TFLOP/s; kernel {kernel_ms:.4f} ms")
+
+    secondary = {}
+    if not args.no_secondary:
+        for name in ("square_1024", "ragged_4000x11000x4100", "skinny_64x16384x8192"):
+            sw = inputs.WORKLOADS[name]
+            if sw.name == w.name:
+                continue
+            s_ms, s_kms = time_workload(sw, 50, 10, 3, device)
+            entry = {"ms": round(s_kms, 5), "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
+                     "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
+                     "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}
+            entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
+            secondary[name] = entry
+            log(f"[bench] {name}: {entry}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {cpu}")
+        cpu.pop("seconds", None)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "accumulate": "fp32",
+                   "input_dist": f"N(0,1)*{w.scale}", "kernel": binding.CONFIG_NAMES.get(cfg["config_id"]),
+                   "block": [cfg["block_m"], cfg["block_n"], cfg["block_k"]], "stages": cfg["stages"],
+                   "grid": cfg["grid"], "rotated_sets": args.sets},
+        "frac_of_peak": round(tflops / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kernel_tflops / peak, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

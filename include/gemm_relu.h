@@ -1,0 +1,116 @@
+/*
+ * gemm_relu.h -- C ABI of the MI355X (gfx950) fused GEMM + ReLU library.
+ *
+ * The operation is the GEMM + ReLU example of "Writing High-Performance
+ * Kernels in TileLang" (atlascloud.ai, section "Let's write a GEMM"; also its
+ * Korean edition and the matrix-multiply example of the devpress.csdn.net
+ * TileLang introduction):
+ *
+ *     C[i][j] = cast( max( sum_{k < K} A[i][k] * B[k][j], 0 ) )
+ *
+ * with A of shape (M, K), B of shape (K, N) and C of shape (M, N), all dense
+ * row-major (leading dimensions K, N and N), all of one 16-bit dtype.  Products
+ * are accumulated in fp32; max(x, 0) is taken on the fp32 accumulator and gives
+ * +0.0 for every x <= 0; the cast rounds to nearest, ties to even.  The example
+ * allocates C itself and passes it in; this ABI does the same.
+ *
+ * Memory: A, B and C are device pointers owned by the caller (e.g. torch
+ * allocations).  The library allocates nothing per call and keeps no state
+ * between calls except a per-device cache of the device's architecture.
+ *
+ * Streams: work is enqueued on `stream` (a hipStream_t; NULL means the null
+ * stream) and the call returns without waiting.  C is complete once the
+ * stream has been synchronised.  Calls on different streams that write the
+ * same C race.
+ *
+ * Errors: every argument is checked before anything is launched; on an error
+ * the return value is negative, nothing is launched and C is not touched.
+ *
+ * Limits: M, N, K >= 0; M, N <= 2^24, K <= 2^22; each of A, B and C must be
+ * smaller than 2^31 bytes in a single 256-row, 64-k-row band (see
+ * GEMM_RELU_ERR_TOO_LARGE); pointers 2-byte aligned.  The fastest kernels also
+ * want K % 8 == 0, N % 8 == 0 and 16-byte aligned A and B; other inputs take
+ * narrower loads, with identical results.
+ */
+#ifndef GEMM_RELU_H
+#define GEMM_RELU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of A, B and C (all three share it). */
+enum {
+    GEMM_RELU_F16 = 0,  /* IEEE binary16 */
+    GEMM_RELU_BF16 = 1  /* bfloat16 */
+};
+
+/* Return codes. */
+enum {
+    GEMM_RELU_OK = 0,
+    GEMM_RELU_ERR_INVALID_ARG = -1, /* null pointer with work to do, negative dimension */
+    GEMM_RELU_ERR_BAD_DTYPE = -2,   /* dtype is neither GEMM_RELU_F16 nor GEMM_RELU_BF16 */
+    GEMM_RELU_ERR_ALIAS = -3,       /* C overlaps A or B */
+    GEMM_RELU_ERR_MISALIGNED = -4,  /* a pointer is not 2-byte aligned */
+    GEMM_RELU_ERR_NO_DEVICE = -5,   /* no current HIP device, or it is not gfx950 */
+    GEMM_RELU_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
+    GEMM_RELU_ERR_TOO_LARGE = -7,   /* a dimension or an addressed band exceeds the limits above */
+    GEMM_RELU_ERR_BAD_CONFIG = -8   /* an unknown kernel configuration id */
+};
+
+/* Kernel configuration ids for gemm_relu_with_config (GEMM_RELU_CONFIG_AUTO
+ * lets the library choose, as gemm_relu does). */
+enum {
+    GEMM_RELU_CONFIG_AUTO = -1,
+    GEMM_RELU_CONFIG_DIRECT = 0,      /* one wave per 32x32 block, operands from global memory */
+    GEMM_RELU_CONFIG_TILE_256 = 1,    /* 256x256x64 block tile, 4 waves, 2 LDS stages */
+    GEMM_RELU_CONFIG_TILE_128 = 2     /* 128x128x64 block tile, 4 waves, 2 LDS stages */
+};
+
+/* What a configuration is, for reports and tests. */
+typedef struct {
+    int config_id;    /* GEMM_RELU_CONFIG_* actually used */
+    int block_m;      /* rows of C per workgroup */
+    int block_n;      /* columns of C per workgroup */
+    int block_k;      /* k depth of one LDS stage (0 for the direct kernel) */
+    int stages;       /* LDS stages (0 for the direct kernel) */
+    int threads;      /* threads per workgroup */
+    int vec_a;        /* elements per global load of A (1, 2, 4 or 8) */
+    int vec_b;        /* elements per global load of B */
+    int64_t grid;     /* workgroups launched */
+    int lds_bytes;    /* LDS per workgroup */
+} gemm_relu_config_t;
+
+/*
+ * C = ReLU(A @ B).  A: (M, K), B: (K, N), C: (M, N), row-major, `dtype`.
+ * M == 0 or N == 0: returns GEMM_RELU_OK and launches nothing.
+ * K == 0: C is filled with +0.0 (the empty sum is 0 and ReLU(0) = +0.0).
+ */
+int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+              void* stream);
+
+/* Same as gemm_relu with a forced kernel configuration (GEMM_RELU_CONFIG_*).
+ * The result is the same for every configuration on integer-valued inputs;
+ * on real-valued inputs the fp32 summation order may differ. */
+int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                          int dtype, int config_id, void* stream);
+
+/* The configuration gemm_relu would use for these arguments (pure host logic:
+ * no device is touched).  `out` may be NULL.  Returns GEMM_RELU_OK or the
+ * error gemm_relu would return for these arguments' shape, dtype or alignment. */
+int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                           int64_t K, int dtype, int config_id, gemm_relu_config_t* out);
+
+/* A static, human-readable description of a return code. */
+const char* gemm_relu_strerror(int code);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gemm_relu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_RELU_H */

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry
+point, and validates arguments before touching a device.  No GPU is needed and
+no kernel is launched: every call below returns from argument checking, or is
+the pure-host configuration query.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_relu_amd as gr
+from tiled_dense_gemm_relu_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_relu.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemm_relu\w*)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gr.load_library()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted([
+        "gemm_relu", "gemm_relu_with_config", "gemm_relu_query_config", "gemm_relu_strerror",
+        "gemm_relu_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_strerror(lib):
+    assert lib.gemm_relu_version() >= 100
+    for code in list(binding.ERRORS) + [-99]:
+        assert isinstance(gr.strerror(code), str) and gr.strerror(code)
+    assert gr.strerror(0) == "ok"
+
+
+# Fake, well separated addresses: the calls below must fail argument checks
+# before any device work, so these are never dereferenced.
+A_PTR, B_PTR, C_PTR = 1 << 32, 2 << 32, 3 << 32
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A_PTR, B_PTR, C_PTR, 4, 4, 4, 7), -2),                 # bad dtype
+    ((A_PTR, B_PTR, C_PTR, -1, 4, 4, 0), -1),                # negative M
+    ((A_PTR, B_PTR, C_PTR, 4, -1, 4, 0), -1),
+    ((A_PTR, B_PTR, C_PTR, 4, 4, -1, 0), -1),
+    ((A_PTR, B_PTR, 0, 4, 4, 4, 0), -1),                     # null C with work to do
+    ((0, B_PTR, C_PTR, 4, 4, 4, 0), -1),                     # null A with K > 0
+    ((A_PTR, 0, C_PTR, 4, 4, 4, 0), -1),
+    ((A_PTR + 1, B_PTR, C_PTR, 4, 4, 4, 0), -4),             # odd address
+    ((A_PTR, B_PTR, C_PTR + 1, 4, 4, 4, 1), -4),
+    ((A_PTR, B_PTR, A_PTR + 6, 4, 4, 4, 0), -3),             # C overlaps A
+    ((A_PTR, B_PTR, B_PTR - 8, 4, 4, 4, 0), -3),             # C overlaps B
+    ((A_PTR, B_PTR, C_PTR, (1 << 24) + 1, 4, 4, 0), -7),     # beyond the size limits
+    ((A_PTR, B_PTR, C_PTR, 4, 4, (1 << 22) + 1, 0), -7),
+])
+def test_invalid_arguments_are_rejected_before_launch(lib, args, code):
+    a, b, c, M, N, K, dt = args
+    assert lib.gemm_relu(a, b, c, M, N, K, dt, None) == code
+    assert lib.gemm_relu_query_config(a, b, c, M, N, K, dt, -1, None) == code
+
+
+def test_unknown_config_is_rejected(lib):
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 3, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
+
+
+def test_empty_outputs_are_a_no_op(lib):
+    # M == 0 or N == 0: nothing to write, OK without touching a device (null pointers allowed).
+    assert lib.gemm_relu(0, 0, 0, 0, 5, 5, 0, None) == 0
+    assert lib.gemm_relu(0, 0, 0, 5, 0, 5, 1, None) == 0
+
+
+def test_k_zero_needs_no_inputs():
+    cfg = gr.selected_config(3, 5, 0, a_ptr=0, b_ptr=0)
+    assert cfg["grid"] >= 1 and cfg["threads"] == 256
+
+
+def test_config_choice_for_the_workload_shapes():
+    big = gr.selected_config(8192, 8192, 8192)
+    assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (1, 256, 256, 64)
+    assert (big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (8, 8, 1024, 131072)
+    small = gr.selected_config(1024, 1024, 1024)
+    assert (small["config_id"], small["block_m"], small["grid"]) == (2, 128, 64)
+    ragged = gr.selected_config(4000, 11000, 4100)
+    assert ragged["config_id"] == 1 and ragged["grid"] == 16 * 43
+    assert (ragged["vec_a"], ragged["vec_b"]) == (4, 8)             # K % 8 == 4: 8-byte A loads
+    skinny = gr.selected_config(64, 16384, 8192, dtype=gr.BF16)
+    assert skinny["grid"] >= 128
+
+
+@pytest.mark.parametrize("K,N,a_off,b_off,want", [
+    (8, 8, 0, 0, (8, 8)), (12, 8, 0, 0, (4, 8)), (8, 12, 0, 0, (8, 4)), (6, 6, 0, 0, (2, 2)),
+    (7, 8, 0, 0, (1, 1)), (8, 8, 8, 0, (4, 8)), (8, 8, 2, 2, (1, 1)),
+])
+def test_load_width_follows_row_length_and_alignment(K, N, a_off, b_off, want):
+    cfg = gr.selected_config(512, N, K, config=1, a_ptr=4096 + a_off, b_ptr=(1 << 20) + b_off)
+    assert (cfg["vec_a"], cfg["vec_b"]) == want
+
+
+def test_direct_config_geometry():
+    cfg = gr.selected_config(100, 70, 9, config=0)
+    assert (cfg["block_m"], cfg["block_n"], cfg["threads"], cfg["grid"]) == (32, 32, 64, 4 * 3)

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars:
+- integer-valued inputs (entries in {-2..2}): every fp32 partial sum is an exact
+  integer, so the GPU result must equal the oracle's bit for bit;
+- real-valued inputs: |C_gpu - C_ref| <= 1e-2 + 1e-2 * |C_ref| elementwise
+  (the acceptance rule of the GEMM + ReLU example in "Writing High-Performance
+  Kernels in TileLang", section "Let's write a GEMM": rtol = atol = 1e-2);
+- always: C >= 0, no -0.0, no NaN; nothing written outside C.
+
+Full-size workloads the oracle cannot finish in seconds are checked on sampled
+rows (each a complete row of C, spread over first, middle and last tiles) and
+sampled elements, in the launch configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_dense_gemm_relu_amd as gr
+from tiled_dense_gemm_relu_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL = ATOL = 1e-2
+CONFIGS = [binding.CONFIG_DIRECT, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128]
+DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def values(b: np.ndarray, dtype) -> np.ndarray:
+    return torch.from_numpy(b.view(np.int16)).view(DT[dtype]).to(torch.float64).numpy()
+
+
+def run_gpu(a, b, config=binding.CONFIG_AUTO):
+    c = gr.gemm_relu(a.cuda(), b.cuda(), config=config)
+    torch.cuda.synchronize()
+    return bits(c)
+
+
+def check_relu_invariants(got_bits, dtype):
+    v = values(got_bits, dtype)
+    assert not np.isnan(v).any(), "NaN in output"
+    assert (v >= 0).all(), "negative output"
+    assert not (got_bits == 0x8000).any(), "-0.0 in output"
+
+
+def assert_within_tolerance(got_bits, want_bits, dtype):
+    g, w = values(got_bits, dtype), values(want_bits, dtype)
+    err = np.abs(g - w)
+    bound = ATOL + RTOL * np.abs(w)
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} elements out of tolerance; worst at "
+                           f"{np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+# ------------------------------------------------------------- integer inputs
+
+INT_SHAPES = [(1, 1, 1), (32, 32, 16), (33, 65, 17), (255, 257, 63), (257, 255, 65),
+              (300, 520, 130), (129, 131, 200), (512, 256, 192), (64, 1000, 1024)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("config", CONFIGS)
+@pytest.mark.parametrize("shape", INT_SHAPES)
+def test_integer_inputs_bit_exact(shape, config, dtype):
+    M, N, K = shape
+    a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=M + 7 * N + 13 * K)
+    want = oracle.gemm_relu(a, b, dtype)
+    got = run_gpu(a, b, config)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_small_256_workload(config):
+    w = inputs.WORKLOADS["small_256"]
+    for integer in (False, True):
+        a, b = inputs.workload_inputs(w, integer)
+        want = oracle.gemm_relu(a, b, w.dtype)
+        got = run_gpu(a, b, config)
+        check_relu_invariants(got, w.dtype)
+        if integer:
+            assert np.array_equal(got, want)
+        else:
+            assert_within_tolerance(got, want, w.dtype)
+
+
+@pytest.mark.parametrize("config", [binding.CONFIG_AUTO, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128])
+def test_square_1024_workload(config):
+    w = inputs.WORKLOADS["square_1024"]
+    for integer in (False, True):
+        a, b = inputs.workload_inputs(w, integer)
+        want = oracle.gemm_relu(a, b, w.dtype)
+        got = run_gpu(a, b, config)
+        check_relu_invariants(got, w.dtype)
+        if integer:
+            assert np.array_equal(got, want)
+        else:
+            assert_within_tolerance(got, want, w.dtype)
+
+
+# ------------------------------------------------------- full-size workloads
+
+
+def sample_rows(M, tile=256):
+    rows = {0, 1, M // 2, M - 2, M - 1}
+    last_tile = (M - 1) // tile * tile
+    rows |= {tile - 1, tile, last_tile, min(M - 1, last_tile + 1)}
+    return sorted(r for r in rows if 0 <= r < M)
+
+
+def check_sampled(w, integer, n_entries=2048):
+    a, b = inputs.workload_inputs(w, integer)
+    say(f"[{w.name} integer={integer}] GPU run")
+    c = gr.gemm_relu(a.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    got = bits(c)
+    check_relu_invariants(got, w.dtype)
+    rows = sample_rows(w.M)
+    say(f"[{w.name} integer={integer}] oracle on rows {rows}")
+    want_rows = np.concatenate([oracle.gemm_relu_rows(a, b, w.dtype, r, r + 1) for r in rows])
+    rng = np.random.default_rng(w.seed)
+    ii, jj = rng.integers(0, w.M, n_entries), rng.integers(0, w.N, n_entries)
+    want_entries = oracle.gemm_relu_entries(a, b, w.dtype, ii, jj)
+    if integer:
+        assert np.array_equal(got[rows], want_rows)
+        assert np.array_equal(got[ii, jj], want_entries)
+    else:
+        assert_within_tolerance(got[rows], want_rows, w.dtype)
+        assert_within_tolerance(got[ii, jj], want_entries, w.dtype)
+    return got
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_ragged_4000x11000x4100_sampled(integer):
+    w = inputs.WORKLOADS["ragged_4000x11000x4100"]
+    got = check_sampled(w, integer)
+    if not integer:
+        frac_zero = (got == 0).mean()
+        assert 0.4 < frac_zero < 0.6                # about half the sums are negative
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_square_8192_sampled(integer):
+    w = inputs.WORKLOADS["square_8192"]
+    got = check_sampled(w, integer, n_entries=1024)
+    if not integer:
+        assert 0.45 < (got == 0).mean() < 0.55
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_skinny_64x16384x8192_bf16_full(integer):
+    w = inputs.WORKLOADS["skinny_64x16384x8192"]
+    a, b = inputs.workload_inputs(w, integer)
+    got = run_gpu(a, b)
+    say(f"[{w.name} integer={integer}] full oracle")
+    want = oracle.gemm_relu(a, b, w.dtype)
+    check_relu_invariants(got, w.dtype)
+    if integer:
+        assert np.array_equal(got, want)
+    else:
+        assert_within_tolerance(got, want, w.dtype)
+
+
+# ------------------------------------------------------------------ edge cases
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_k_zero_fills_positive_zero(config):
+    a = torch.empty((37, 0), dtype=torch.float16, device="cuda")
+    b = torch.empty((0, 53), dtype=torch.float16, device="cuda")
+    c = torch.full((37, 53), float("nan"), dtype=torch.float16, device="cuda")
+    gr.gemm_relu(a, b, out=c, config=config)
+    torch.cuda.synchronize()
+    assert (bits(c) == 0).all()
+
+
+def test_empty_m_or_n():
+    a = torch.empty((0, 16), dtype=torch.float16, device="cuda")
+    b = torch.ones((16, 8), dtype=torch.float16, device="cuda")
+    assert gr.gemm_relu(a, b).shape == (0, 8)
+    a = torch.ones((4, 16), dtype=torch.float16, device="cuda")
+    b = torch.empty((16, 0), dtype=torch.float16, device="cuda")
+    assert gr.gemm_relu(a, b).shape == (4, 0)
+
+
+@pytest.mark.parametrize("a_off,b_off,c_off", [(1, 0, 0), (0, 1, 0), (0, 0, 1), (3, 5, 7), (4, 4, 0)])
+@pytest.mark.parametrize("config", CONFIGS)
+def test_unaligned_pointers(a_off, b_off, c_off, config):
+    # Views starting a few elements into a buffer: 2-byte aligned only.
+    M, N, K = 130, 270, 100
+    a, b = inputs.integer_pair(M, N, K, torch.float16, seed=99)
+    want = oracle.gemm_relu(a, b, "fp16")
+    abuf = torch.zeros(M * K + a_off, dtype=torch.float16, device="cuda")
+    bbuf = torch.zeros(K * N + b_off, dtype=torch.float16, device="cuda")
+    cbuf = torch.zeros(M * N + c_off, dtype=torch.float16, device="cuda")
+    av = abuf[a_off:].view(M, K)
+    bv = bbuf[b_off:].view(K, N)
+    cv = cbuf[c_off:].view(M, N)
+    av.copy_(a)
+    bv.copy_(b)
+    gr.gemm_relu(av, bv, out=cv, config=config)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(cv), want)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 7, 9, 63, 65, 127])
+def test_odd_k(K):
+    M, N = 70, 90
+    for dtype in ("fp16", "bf16"):
+        a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=K)
+        want = oracle.gemm_relu(a, b, dtype)
+        for config in CONFIGS:
+            assert np.array_equal(run_gpu(a, b, config), want), (dtype, config)
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_nothing_written_outside_c(config):
+    M, N, K = 250, 300, 70
+    guard = 4096
+    a, b = inputs.normal_pair(M, N, K, torch.float16, 1.0, 5)
+    buf = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+    c = buf[guard:guard + M * N].view(M, N)
+    gr.gemm_relu(a.cuda(), b.cuda(), out=c, config=config)
+    torch.cuda.synchronize()
+    raw = bits(buf)
+    nan_bits = bits(torch.tensor([float("nan")], dtype=torch.float16))[0]
+    assert (raw[:guard] == nan_bits).all() and (raw[guard + M * N:] == nan_bits).all()
+    assert_within_tolerance(raw[guard:guard + M * N].reshape(M, N), oracle.gemm_relu(a, b, "fp16"), "fp16")
+
+
+def test_run_to_run_bit_identical():
+    w = inputs.WORKLOADS["ragged_4000x11000x4100"]
+    a, b = inputs.workload_inputs(w)
+    a, b = a.cuda(), b.cuda()
+    c1 = bits(gr.gemm_relu(a, b))
+    c2 = bits(gr.gemm_relu(a, b))
+    assert np.array_equal(c1, c2)
+
+
+def test_all_configs_agree_on_integer_inputs():
+    a, b = inputs.integer_pair(777, 555, 333, torch.bfloat16, seed=4)
+    outs = [run_gpu(a, b, cfg) for cfg in CONFIGS]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_side_stream():
+    a, b = inputs.integer_pair(300, 200, 100, torch.float16, seed=8)
+    want = oracle.gemm_relu(a, b, "fp16")
+    s = torch.cuda.Stream()
+    a, b = a.cuda(), b.cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = gr.gemm_relu(a, b)
+    s.synchronize()
+    assert np.array_equal(bits(c), want)
+
+
+def test_alias_is_rejected_and_c_untouched():
+    a = torch.ones((64, 64), dtype=torch.float16, device="cuda")
+    b = torch.ones((64, 64), dtype=torch.float16, device="cuda")
+    before = bits(a).copy()
+    with pytest.raises(binding.GemmReluError) as e:
+        gr.gemm_relu(a, b, out=a)
+    assert e.value.code == -3
+    assert np.array_equal(bits(a), before)
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    a = torch.ones((4, 8), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        gr.gemm_relu(a, a)                                  # inner dims differ
+    with pytest.raises(ValueError):
+        gr.gemm_relu(a.t(), a.t().contiguous())             # non-contiguous
+    with pytest.raises(TypeError):
+        gr.gemm_relu(a.float(), a.t().contiguous().float())
+    with pytest.raises(ValueError):
+        gr.gemm_relu(a.cpu(), a.t().contiguous().cpu())

@@ -1,6 +1,149 @@
-"""placeholder"""
-F16, BF16 = 0, 1
+"""Thin ctypes binding over libgemm_relu.so (the C ABI in include/gemm_relu.h).
+
+Argument marshalling only: every step of ReLU(A @ B) runs in the library's
+HIP kernels.  torch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+F16 = 0
+BF16 = 1
+
+CONFIG_AUTO = -1
+CONFIG_DIRECT = 0
+CONFIG_TILE_256 = 1
+CONFIG_TILE_128 = 2
+CONFIG_NAMES = {CONFIG_DIRECT: "direct_32x32", CONFIG_TILE_256: "tile_256x256x64",
+                CONFIG_TILE_128: "tile_128x128x64"}
+
+ERRORS = {
+    0: "OK", -1: "INVALID_ARG", -2: "BAD_DTYPE", -3: "ALIAS", -4: "MISALIGNED", -5: "NO_DEVICE",
+    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG",
+}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
+_lock = threading.Lock()
+_lib = None
+
+
 class GemmReluError(RuntimeError):
-    pass
-def gemm_relu(*a, **k): raise NotImplementedError
-gemm_relu_raw = selected_config = strerror = library_path = load_library = gemm_relu
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gemm_relu failed: {ERRORS.get(code, code)} ({code}): {msg}")
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("config_id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("threads", ctypes.c_int),
+                ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int), ("grid", ctypes.c_int64),
+                ("lds_bytes", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgemm_relu.so (built in-tree by tiled_dense_gemm_relu_amd.build); raise if absent."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                                   "`python -m tiled_dense_gemm_relu_amd.build` (needs hipcc)")
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            lib.gemm_relu.argtypes = [vp, vp, vp, i64, i64, i64, ci, vp]
+            lib.gemm_relu.restype = ci
+            lib.gemm_relu_with_config.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+            lib.gemm_relu_with_config.restype = ci
+            lib.gemm_relu_query_config.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ctypes.POINTER(_Config)]
+            lib.gemm_relu_query_config.restype = ci
+            lib.gemm_relu_strerror.argtypes = [ci]
+            lib.gemm_relu_strerror.restype = ctypes.c_char_p
+            lib.gemm_relu_version.argtypes = []
+            lib.gemm_relu_version.restype = ci
+            _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().gemm_relu_strerror(code).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise GemmReluError(code, strerror(code))
+
+
+def gemm_relu_raw(a_ptr: int, b_ptr: int, c_ptr: int, M: int, N: int, K: int, dtype: int,
+                  stream: int = 0, config: int = CONFIG_AUTO) -> int:
+    """Call the C ABI with raw device pointers; returns the library's status code."""
+    lib = load_library()
+    if config == CONFIG_AUTO:
+        return lib.gemm_relu(a_ptr, b_ptr, c_ptr, M, N, K, dtype, stream or None)
+    return lib.gemm_relu_with_config(a_ptr, b_ptr, c_ptr, M, N, K, dtype, config, stream or None)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"gemm_relu: dtype must be float16 or bfloat16, got {t.dtype}")
+
+
+def _check_tensors(a, b, out):
+    import torch
+    for name, t in (("a", a), ("b", b)) + ((("out", out),) if out is not None else ()):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"gemm_relu: {name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"gemm_relu: {name} must be a GPU tensor, got {t.device}")
+        if t.dim() != 2:
+            raise ValueError(f"gemm_relu: {name} must be 2-D, got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"gemm_relu: {name} must be contiguous (row-major)")
+    if a.dtype != b.dtype or (out is not None and out.dtype != a.dtype):
+        raise TypeError("gemm_relu: a, b and out must share one dtype")
+    if a.shape[1] != b.shape[0]:
+        raise ValueError(f"gemm_relu: inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    if a.device != b.device or (out is not None and out.device != a.device):
+        raise ValueError("gemm_relu: a, b and out must be on one device")
+    if out is not None and tuple(out.shape) != (a.shape[0], b.shape[1]):
+        raise ValueError(f"gemm_relu: out must have shape {(a.shape[0], b.shape[1])}, got {tuple(out.shape)}")
+
+
+def gemm_relu(a, b, out=None, config: int = CONFIG_AUTO, stream=None):
+    """C = ReLU(a @ b) for row-major fp16/bf16 GPU tensors a (M, K) and b (K, N).
+
+    ``out`` (M, N) is written if given, else allocated.  The kernel is enqueued
+    on ``stream`` (a torch.cuda.Stream), by default torch's current stream.
+    """
+    import torch
+    _check_tensors(a, b, out)
+    dtype = _dtype_code(a)
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        rc = gemm_relu_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, s.cuda_stream, config)
+    _check(rc)
+    return out
+
+
+def selected_config(M: int, N: int, K: int, dtype: int = F16, config: int = CONFIG_AUTO,
+                    a_ptr: int = 256, b_ptr: int = 256, c_ptr: int = 1 << 40) -> dict:
+    """The kernel configuration the library would pick (host logic only, no device needed)."""
+    cfg = _Config()
+    rc = load_library().gemm_relu_query_config(a_ptr, b_ptr, c_ptr, M, N, K, dtype, config, ctypes.byref(cfg))
+    _check(rc)
+    return {f: getattr(cfg, f) for f, _ in _Config._fields_}

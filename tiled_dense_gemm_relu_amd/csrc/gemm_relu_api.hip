@@ -1,0 +1,230 @@
+// C ABI of the gfx950 GEMM + ReLU library: argument checks, kernel choice and
+// launch.  The operation and its contract are documented in gemm_relu.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/gemm_relu.h"
+#include "kernel_table.hpp"
+
+namespace gemm_relu_hip {
+namespace {
+
+constexpr int kVersion = 100;                    // 0.1.0
+constexpr int64_t kMaxMN = int64_t(1) << 24;
+constexpr int64_t kMaxK = int64_t(1) << 22;
+constexpr int64_t kMaxBand = (int64_t(1) << 31) - 1;   // bytes one buffer descriptor may address
+constexpr int kDirectTile = 32;
+
+struct Plan {
+    gemm_relu_config_t cfg;
+    int tile;          // TileId, or -1 for the direct kernel, -2 for the K == 0 fill
+    int vec_pair;      // index into kVecPairs
+    int tiles_m, tiles_n;
+    int c_vec_ok;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest of 8, 4, 2, 1 elements that divides the row length and the pointer's
+// alignment (in 2-byte elements).
+int vec_width(const void* p, int64_t row_len)
+{
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
+    for (int v = 8; v > 1; v /= 2)
+        if (row_len % v == 0 && addr % (uintptr_t)(2 * v) == 0) return v;
+    return 1;
+}
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes)
+{
+    if (a_bytes <= 0 || b_bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+// Every check that needs no device.  Fills `plan` on success.
+int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K, int dtype,
+              int config_id, Plan* plan)
+{
+    if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
+    if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_TILE_128)
+        return GEMM_RELU_ERR_BAD_CONFIG;
+    if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
+
+    std::memset(plan, 0, sizeof(*plan));
+    plan->cfg.config_id = config_id;
+    plan->tile = -3;
+    if (M == 0 || N == 0) return GEMM_RELU_OK;        // nothing to compute or write
+
+    const bool need_c = true;
+    const bool need_ab = K > 0;
+    if ((need_c && !C) || (need_ab && (!A || !B))) return GEMM_RELU_ERR_INVALID_ARG;
+    const uintptr_t odd = reinterpret_cast<uintptr_t>(C) | (need_ab ? (reinterpret_cast<uintptr_t>(A) |
+                                                                      reinterpret_cast<uintptr_t>(B))
+                                                                   : 0);
+    if (odd & 1) return GEMM_RELU_ERR_MISALIGNED;
+    const int64_t a_bytes = need_ab ? 2 * M * K : 0, b_bytes = need_ab ? 2 * K * N : 0;
+    const int64_t c_bytes = 2 * M * N;
+    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)) return GEMM_RELU_ERR_ALIAS;
+
+    const uintptr_t c_addr = reinterpret_cast<uintptr_t>(C);
+    plan->c_vec_ok = (N % 4 == 0 && c_addr % 8 == 0) ? 1 : 0;
+
+    if (K == 0) {
+        plan->tile = -2;
+        plan->cfg.config_id = config_id;
+        plan->cfg.threads = 256;
+        plan->cfg.grid = std::min<int64_t>(ceil_div(M * N, 256), 65536);
+        return GEMM_RELU_OK;
+    }
+
+    int chosen = config_id;
+    if (chosen == GEMM_RELU_CONFIG_AUTO) {
+        // The 256x256 tile when it yields enough workgroups to cover the 256
+        // CUs a few times over; otherwise the 128x128 tile (4x the workgroups).
+        const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+        chosen = t256 >= 192 ? GEMM_RELU_CONFIG_TILE_256 : GEMM_RELU_CONFIG_TILE_128;
+    }
+    plan->cfg.config_id = chosen;
+
+    if (chosen == GEMM_RELU_CONFIG_DIRECT) {
+        const int64_t tm = ceil_div(M, kDirectTile), tn = ceil_div(N, kDirectTile);
+        if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
+        plan->tile = -1;
+        plan->tiles_m = (int)tm;
+        plan->tiles_n = (int)tn;
+        plan->cfg.block_m = kDirectTile;
+        plan->cfg.block_n = kDirectTile;
+        plan->cfg.threads = 64;
+        plan->cfg.vec_a = 1;
+        plan->cfg.vec_b = 1;
+        plan->cfg.grid = tm * tn;
+        return GEMM_RELU_OK;
+    }
+
+    const int tile = chosen == GEMM_RELU_CONFIG_TILE_256 ? kTile256 : kTile128;
+    const TileGeom& g = kTileGeom[tile];
+    // Each workgroup addresses A through a descriptor over bm rows and B through
+    // one over bk rows; both must stay below 2^31 bytes.
+    if (int64_t(g.bm) * K * 2 > kMaxBand || int64_t(g.bk) * N * 2 > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
+    const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
+    if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
+
+    const int va = vec_width(A, K), vb = vec_width(B, N);
+    int pair = kNumVecPairs - 1;
+    for (int i = 0; i < kNumVecPairs; ++i)
+        if (kVecPairs[i][0] <= va && kVecPairs[i][1] <= vb) { pair = i; break; }
+
+    plan->tile = tile;
+    plan->vec_pair = pair;
+    plan->tiles_m = (int)tm;
+    plan->tiles_n = (int)tn;
+    plan->cfg.block_m = g.bm;
+    plan->cfg.block_n = g.bn;
+    plan->cfg.block_k = g.bk;
+    plan->cfg.stages = g.stages;
+    plan->cfg.threads = g.threads;
+    plan->cfg.vec_a = kVecPairs[pair][0];
+    plan->cfg.vec_b = kVecPairs[pair][1];
+    plan->cfg.grid = tm * tn;
+    plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2;
+    return GEMM_RELU_OK;
+}
+
+// Per-device cache: 0 unknown, 1 gfx950, -1 something else.
+std::atomic<int> g_device_ok[64];
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_RELU_ERR_NO_DEVICE;
+    if (dev < 64) {
+        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known != 0) return known > 0 ? GEMM_RELU_OK : GEMM_RELU_ERR_NO_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_RELU_ERR_NO_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? GEMM_RELU_OK : GEMM_RELU_ERR_NO_DEVICE;
+}
+
+int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+           hipStream_t stream)
+{
+    const DtypeKernels& ks = dtype == GEMM_RELU_F16 ? kernels_f16() : kernels_bf16();
+    int m = (int)M, n = (int)N, k = (int)K;
+    hipError_t err;
+    if (p.tile == -2) {
+        size_t count = (size_t)M * (size_t)N;
+        void* args[] = {&C, &count};
+        err = hipLaunchKernel(zero_fill_kernel(), dim3((unsigned)p.cfg.grid), dim3(256), args, 0, stream);
+    } else if (p.tile == -1) {
+        int tiles_m = p.tiles_m, c_vec_ok = p.c_vec_ok;
+        void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &c_vec_ok};
+        err = hipLaunchKernel(ks.direct, dim3((unsigned)p.cfg.grid), dim3(64), args, 0, stream);
+    } else {
+        int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
+        void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
+        err = hipLaunchKernel(ks.tiled[p.tile][p.vec_pair], dim3((unsigned)p.cfg.grid),
+                              dim3((unsigned)p.cfg.threads), args, 0, stream);
+    }
+    return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace gemm_relu_hip
+
+using namespace gemm_relu_hip;
+
+extern "C" {
+
+int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                           int dtype, int config_id, gemm_relu_config_t* out)
+{
+    Plan p;
+    const int rc = make_plan(A, B, C, M, N, K, dtype, config_id, &p);
+    if (rc == GEMM_RELU_OK && out) *out = p.cfg;
+    return rc;
+}
+
+int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                          int config_id, void* stream)
+{
+    Plan p;
+    int rc = make_plan(A, B, C, M, N, K, dtype, config_id, &p);
+    if (rc != GEMM_RELU_OK) return rc;
+    if (p.tile == -3) return GEMM_RELU_OK;          // M == 0 or N == 0
+    rc = check_device();
+    if (rc != GEMM_RELU_OK) return rc;
+    return launch(p, A, B, C, M, N, K, dtype, static_cast<hipStream_t>(stream));
+}
+
+int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype, void* stream)
+{
+    return gemm_relu_with_config(A, B, C, M, N, K, dtype, GEMM_RELU_CONFIG_AUTO, stream);
+}
+
+const char* gemm_relu_strerror(int code)
+{
+    switch (code) {
+    case GEMM_RELU_OK: return "ok";
+    case GEMM_RELU_ERR_INVALID_ARG: return "invalid argument (null pointer or negative dimension)";
+    case GEMM_RELU_ERR_BAD_DTYPE: return "unsupported dtype (expected GEMM_RELU_F16 or GEMM_RELU_BF16)";
+    case GEMM_RELU_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_RELU_ERR_MISALIGNED: return "pointer not 2-byte aligned";
+    case GEMM_RELU_ERR_NO_DEVICE: return "no current HIP device, or the device is not gfx950";
+    case GEMM_RELU_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_RELU_ERR_TOO_LARGE: return "dimensions exceed the supported range";
+    case GEMM_RELU_ERR_BAD_CONFIG: return "unknown kernel configuration id";
+    default: return "unknown error code";
+    }
+}
+
+int gemm_relu_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,400 @@
+// gfx950 (CDNA4) kernels for C = ReLU(A @ B).
+//
+// A is (M, K), B is (K, N), C is (M, N), all row-major, one 16-bit dtype
+// (fp16 or bf16); products accumulate in fp32 registers, ReLU is applied to the
+// fp32 accumulator and the result is rounded to nearest even into the dtype of
+// C.  This is the GEMM + ReLU example of "Writing High-Performance Kernels in
+// TileLang" (atlascloud.ai, section "Let's write a GEMM"): a block tile of C
+// per workgroup, A and B tiles staged through shared memory in a multi-stage
+// software pipeline, a tile-level matrix-core product into an fp32 fragment,
+// an elementwise max(x, 0) on the fragment, a cast and a store.
+//
+// What changes for CDNA4:
+//  * The contraction runs on v_mfma_f32_32x32x16_{f16,bf16}: one wave64
+//    computes a 32x32 fp32 block per instruction from two 16-byte operand
+//    fragments per lane.  Both operands want 8 consecutive k values per lane.
+//  * B arrives N-contiguous, so it is transposed on its way into LDS (two
+//    v_perm_b32 per pair of halves), which leaves both LDS tiles K-contiguous:
+//    every operand fragment is then a single ds_read_b128.
+//  * The MFMA "A" operand is the B^T tile and the "B" operand is the A tile,
+//    so the MFMA output block is C^T: each lane then owns 4 consecutive
+//    columns of one row of C and stores them with one 8-byte store.
+//  * LDS rows are 128 bytes (BK = 64 halves = 8 chunks of 16 bytes).  The
+//    16-byte chunk c of row r sits at chunk position c ^ ((r ^ (r >> 3)) & 7).
+//    The XOR swizzle is the idea of "TileLang Guide: Composable Tiled AI Kernel
+//    Programming" (section "Automated Layout Inference and Bank Conflict
+//    Elimination") and of the zwxr.cn hands-on article, section 2.3 (shared
+//    memory and bank conflicts); this particular function is chosen for
+//    ds_read_b128 reading 16 consecutive rows at one logical chunk, which it
+//    spreads over 16 distinct 16-byte bank groups (a 256-byte bank window).
+//  * Global loads are buffer loads whose descriptor covers only the rows that
+//    exist: rows past M (for A) or past K (for B) read as zero in hardware;
+//    columns past K (A) or past N (B) are masked by sending the offset out of
+//    range.  This is the M/N/K tail handling.
+//  * Workgroup ids are remapped so that each of the 8 XCDs (each with its own
+//    L2) gets a contiguous range of tiles, and tiles are visited in panels of
+//    GROUP_M tile-rows (the rasterization of T.use_swizzle in the pages'
+//    listing, re-derived for XCD round-robin dispatch).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm_relu_hip {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum Dtype { kF16 = 0, kBF16 = 1 };
+
+// Buffer descriptor word 3 for gfx9-family raw buffers (32-bit data format,
+// no swizzle, range checking on).
+constexpr int kBufferFlags = 0x00020000;
+// An offset that is always beyond every descriptor's num_records: loads from it
+// return zero.  The host guarantees num_records < 2^31.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+template <int DT>
+__device__ __forceinline__ floatx16 mfma_32x32x16(u32x4 a, u32x4 b, floatx16 c)
+{
+    if constexpr (DT == kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                      __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ReLU on the fp32 accumulator, then round to nearest even into the dtype.
+// x > 0 ? x : 0 (a select, not fmax) so that every x <= 0 gives +0.0.
+template <int DT>
+__device__ __forceinline__ uint16_t relu_cast(float x)
+{
+    float r = x > 0.0f ? x : 0.0f;
+    if constexpr (DT == kF16)
+        return __builtin_bit_cast(uint16_t, (_Float16)r);
+    else
+        return __builtin_bit_cast(uint16_t, (__bf16)r);
+}
+
+// ---------------------------------------------------------------- rasterization
+
+// Map the hardware workgroup id to a (tile_m, tile_n) pair.
+//  1. XCD remap: the dispatcher hands workgroup w to XCD w % 8.  Logical id
+//     (w % 8) * (T / 8) + w / 8 gives XCD x the contiguous logical range
+//     [x * T/8, (x+1) * T/8), so tiles that share A/B panels share one L2.
+//     Ids past the last multiple of 8 keep their own number (a bijection).
+//  2. Panels: logical ids walk GROUP_M tile-rows at a time, column by column
+//     inside the panel, so the tiles in flight reuse the same few A row-panels
+//     and B column-panels.
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int group_m,
+                                            int& tm, int& tn)
+{
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = total / 8;
+    int pid = wg;
+    if (wg < per_xcd * 8) pid = (wg % 8) * per_xcd + wg / 8;
+    const int panel = group_m * tiles_n;
+    const int first_m = (pid / panel) * group_m;
+    const int rows = min(tiles_m - first_m, group_m);
+    const int in_panel = pid % panel;
+    tm = first_m + in_panel % rows;
+    tn = in_panel / rows;
+}
+
+// ---------------------------------------------------------------- global loads
+
+// Load 8 consecutive 16-bit elements starting at byte offset `off` of the
+// buffer, as VEC-element pieces; piece p is read only if valid(p) and is zero
+// otherwise.  VEC divides the row length, so a piece is all in or all out.
+template <int VEC, class Valid>
+__device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rsrc, uint32_t off, Valid valid)
+{
+    if constexpr (VEC == 8) {
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, valid(0) ? off : kOobOffset, 0, 0);
+    } else if constexpr (VEC == 4) {
+        u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rsrc, valid(0) ? off : kOobOffset, 0, 0);
+        u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(rsrc, valid(1) ? off + 8 : kOobOffset, 0, 0);
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else if constexpr (VEC == 2) {
+        u32x4 r;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            r[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, valid(p) ? off + 4 * p : kOobOffset, 0, 0);
+        return r;
+    } else {
+        static_assert(VEC == 1, "VEC must be 1, 2, 4 or 8");
+        uint32_t h[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            h[p] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, valid(p) ? off + 2 * p : kOobOffset, 0, 0);
+        return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+}
+
+// ---------------------------------------------------------------- LDS layout
+
+// Byte offset of logical 16-byte chunk c (0..7) of row r in a 128-byte-row tile.
+__device__ __forceinline__ uint32_t lds_off(int r, int c)
+{
+    return (uint32_t)(r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4));
+}
+
+// ---------------------------------------------------------------- epilogue
+
+// Store the ReLU'd fp32 values of one MFMA output block.  `acc` is the 32x32
+// block of C^T at (n_base .. n_base+31, m_base .. m_base+31): lane l, register
+// 4q + e holds C[m_base + l % 32][n_base + 8q + 4(l / 32) + e].
+template <int DT>
+__device__ __forceinline__ void store_block(uint16_t* __restrict__ C, const floatx16& acc, int lane,
+                                            int m_base, int n_base, int M, int N, bool vec_ok)
+{
+    const int m = m_base + (lane & 31);
+    if (m >= M) return;
+    uint16_t* crow = C + (size_t)m * (size_t)N;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int n = n_base + 8 * q + 4 * (lane >> 5);
+        uint16_t h0 = relu_cast<DT>(acc[4 * q + 0]);
+        uint16_t h1 = relu_cast<DT>(acc[4 * q + 1]);
+        uint16_t h2 = relu_cast<DT>(acc[4 * q + 2]);
+        uint16_t h3 = relu_cast<DT>(acc[4 * q + 3]);
+        if (vec_ok && n + 3 < N) {
+            u32x2 v = {(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
+            *reinterpret_cast<u32x2*>(crow + n) = v;
+        } else {
+            if (n + 0 < N) crow[n + 0] = h0;
+            if (n + 1 < N) crow[n + 1] = h1;
+            if (n + 2 < N) crow[n + 2] = h2;
+            if (n + 3 < N) crow[n + 3] = h3;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- tiled kernel
+
+// BM x BN x 64 block tile, WAVES_M x WAVES_N waves, two LDS stages with the
+// next tile's global loads in flight (in registers) while the current tile's
+// MFMAs run.  VA / VB: elements per global load of A / B (8 needs K % 8 == 0 /
+// N % 8 == 0 and 16-byte aligned base pointers; smaller widths need less).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
+struct TileConfig {
+    static constexpr int BM = BM_;
+    static constexpr int BN = BN_;
+    static constexpr int BK = 64;
+    static constexpr int WAVES_M = WAVES_M_;
+    static constexpr int WAVES_N = WAVES_N_;
+    static constexpr int GROUP_M = GROUP_M_;
+    static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    static constexpr int WTM = BM / WAVES_M;          // wave tile rows (m)
+    static constexpr int WTN = BN / WAVES_N;          // wave tile cols (n)
+    static constexpr int FM = WTM / 32;               // 32x32 MFMA blocks per wave along m
+    static constexpr int FN = WTN / 32;               // ... along n
+    static constexpr int ROW_BYTES = BK * 2;          // 128
+    static constexpr int A_BYTES = BM * ROW_BYTES;
+    static constexpr int B_BYTES = BN * ROW_BYTES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int STAGES = 2;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int A_CHUNKS = BM * (BK / 8) / THREADS;    // 16-byte A chunks per thread
+    static constexpr int KB = BK * BN / 8 / THREADS;            // B rows per thread (x 8 columns)
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert(A_CHUNKS * THREADS == BM * (BK / 8), "A tile must split evenly over threads");
+    static_assert(KB == 8 || KB == 4, "each thread transposes an 8x8 or 4x8 piece of B");
+    static_assert(KB * 8 * THREADS == BK * BN, "B tile must split evenly over threads");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+template <class Cfg, int DT, int VA, int VB>
+__global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    constexpr int THREADS = Cfg::THREADS, KB = Cfg::KB;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / Cfg::WAVES_N;
+    const int wn = wave % Cfg::WAVES_N;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    // A descriptor: rows m0 .. m0 + valid_m - 1 only; later rows read as zero.
+    const int valid_m = min(BM, M - m0);
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        make_rsrc(A + (size_t)m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
+
+    // Per-thread A chunk coordinates (row, logical chunk) inside the tile.
+    int a_row[Cfg::A_CHUNKS], a_chunk[Cfg::A_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_CHUNKS; ++i) {
+        const int q = tid + i * THREADS;
+        a_row[i] = q / (BK / 8);
+        a_chunk[i] = q % (BK / 8);
+    }
+    // Per-thread B piece: rows kb*KB .. +KB-1 of the K tile, columns nb*8 .. +7.
+    const int b_nb = tid % (BN / 8);
+    const int b_kb = tid / (BN / 8);
+    const int b_col = n0 + b_nb * 8;
+    const uint32_t b_off = (uint32_t)(b_kb * KB) * (uint32_t)N * 2u + (uint32_t)b_col * 2u;
+
+    u32x4 ra[Cfg::A_CHUNKS];
+    u32x4 rb[KB];
+
+    auto global_load = [&](int kt) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < Cfg::A_CHUNKS; ++i) {
+            const int kc = k0 + a_chunk[i] * 8;
+            const uint32_t off = (uint32_t)a_row[i] * (uint32_t)K * 2u + (uint32_t)kc * 2u;
+            ra[i] = load_chunk<VA>(rsrc_a, off, [&](int p) { return kc + p * VA < K; });
+        }
+        const int valid_k = min(BK, K - k0);
+        const __amdgpu_buffer_rsrc_t rsrc_b =
+            make_rsrc(B + (size_t)k0 * (size_t)N, (uint32_t)valid_k * (uint32_t)N * 2u);
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+            rb[r] = load_chunk<VB>(rsrc_b, b_off + (uint32_t)r * (uint32_t)N * 2u,
+                                   [&](int p) { return b_col + p * VB < N; });
+    };
+
+    auto lds_store = [&](int stage) {
+        uint8_t* As = smem + stage * Cfg::STAGE_BYTES;
+        uint8_t* Bs = As + Cfg::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < Cfg::A_CHUNKS; ++i)
+            *reinterpret_cast<u32x4*>(As + lds_off(a_row[i], a_chunk[i])) = ra[i];
+        // Transpose the KB x 8 piece of B (rows k, 8 columns n) into 8 rows of
+        // B^T with KB consecutive k each.  Halves n of row k sit in dword n / 2.
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+            const int row = b_nb * 8 + n;
+            if constexpr (KB == 8) {
+                u32x4 v;
+#pragma unroll
+                for (int kp = 0; kp < 4; ++kp)
+                    v[kp] = __builtin_amdgcn_perm(rb[2 * kp + 1][n >> 1], rb[2 * kp][n >> 1], sel);
+                *reinterpret_cast<u32x4*>(Bs + lds_off(row, b_kb)) = v;
+            } else {
+                u32x2 v;
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+                    v[kp] = __builtin_amdgcn_perm(rb[2 * kp + 1][n >> 1], rb[2 * kp][n >> 1], sel);
+                *reinterpret_cast<u32x2*>(Bs + lds_off(row, b_kb >> 1) + (b_kb & 1) * 8) = v;
+            }
+        }
+    };
+
+    floatx16 acc[Cfg::FN][Cfg::FM];
+#pragma unroll
+    for (int i = 0; i < Cfg::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FM; ++j)
+            acc[i][j] = floatx16{0};
+
+    const int KT = (K + BK - 1) / BK;
+    const int frag_row = lane & 31;
+    const int frag_chunk = lane >> 5;
+
+    if (KT > 0) {
+        global_load(0);
+        lds_store(0);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < KT) global_load(kt + 1);
+
+        const uint8_t* As = smem + stage * Cfg::STAGE_BYTES;
+        const uint8_t* Bs = As + Cfg::A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int chunk = ks * 2 + frag_chunk;
+            u32x4 fa[Cfg::FN], fb[Cfg::FM];
+#pragma unroll
+            for (int i = 0; i < Cfg::FN; ++i)
+                fa[i] = *reinterpret_cast<const u32x4*>(Bs + lds_off(wn * Cfg::WTN + i * 32 + frag_row, chunk));
+#pragma unroll
+            for (int j = 0; j < Cfg::FM; ++j)
+                fb[j] = *reinterpret_cast<const u32x4*>(As + lds_off(wm * Cfg::WTM + j * 32 + frag_row, chunk));
+#pragma unroll
+            for (int i = 0; i < Cfg::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FM; ++j)
+                    acc[i][j] = mfma_32x32x16<DT>(fa[i], fb[j], acc[i][j]);
+        }
+
+        if (kt + 1 < KT) lds_store(stage ^ 1);
+        __syncthreads();
+    }
+
+    // Fused epilogue: ReLU, round to the dtype, masked store.
+#pragma unroll
+    for (int i = 0; i < Cfg::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FM; ++j)
+            store_block<DT>(C, acc[i][j], lane, m0 + wm * Cfg::WTM + j * 32, n0 + wn * Cfg::WTN + i * 32,
+                            M, N, c_vec_ok != 0);
+}
+
+// ---------------------------------------------------------------- direct kernel
+
+// One wave per 32x32 block of C, operands gathered straight from global memory
+// with a bounds check per element.  No LDS, no alignment requirement beyond
+// 2 bytes.  It is the general path for shapes the tiled kernels cannot take
+// and a second, structurally different GPU implementation for the tests.
+template <int DT>
+__global__ __launch_bounds__(64) void gemm_relu_direct(const uint16_t* __restrict__ A,
+                                                       const uint16_t* __restrict__ B,
+                                                       uint16_t* __restrict__ C, int M, int N, int K,
+                                                       int tiles_m, int c_vec_ok)
+{
+    const int lane = threadIdx.x;
+    const int tm = blockIdx.x % tiles_m;
+    const int tn = blockIdx.x / tiles_m;
+    const int m = tm * 32 + (lane & 31);
+    const int n = tn * 32 + (lane & 31);
+    const int kg = (lane >> 5) * 8;
+    floatx16 acc = floatx16{0};
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        uint32_t fa[4], fb[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint32_t lo_a = 0, hi_a = 0, lo_b = 0, hi_b = 0;
+            const int k = k0 + kg + 2 * p;
+            if (n < N && k < K) lo_a = B[(size_t)k * N + n];
+            if (n < N && k + 1 < K) hi_a = B[(size_t)(k + 1) * N + n];
+            if (m < M && k < K) lo_b = A[(size_t)m * K + k];
+            if (m < M && k + 1 < K) hi_b = A[(size_t)m * K + k + 1];
+            fa[p] = lo_a | (hi_a << 16);
+            fb[p] = lo_b | (hi_b << 16);
+        }
+        acc = mfma_32x32x16<DT>(u32x4{fa[0], fa[1], fa[2], fa[3]}, u32x4{fb[0], fb[1], fb[2], fb[3]}, acc);
+    }
+    store_block<DT>(C, acc, lane, tm * 32, tn * 32, M, N, c_vec_ok != 0);
+}
+
+// Fill C (M x N) with +0.0: the result for K == 0 (an empty sum is 0, ReLU(0) = 0).
+template <typename T>
+__global__ void gemm_relu_zero_fill(T* __restrict__ C, size_t count)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) C[i] = 0;
+}
+
+}  // namespace gemm_relu_hip

@@ -1,0 +1,33 @@
+// Host-side table of the compiled kernel instances, filled by one translation
+// unit per dtype.  The C ABI (gemm_relu_api.hip) looks kernels up here and
+// launches them with hipLaunchKernel.
+#pragma once
+
+namespace gemm_relu_hip {
+
+// Tile configurations, by GEMM_RELU_CONFIG_* id.
+enum TileId { kTile256 = 0, kTile128 = 1, kNumTiles = 2 };
+
+// Geometry of each tile configuration (must match the TileConfig instances).
+struct TileGeom {
+    int bm, bn, bk, stages, threads, group_m;
+};
+constexpr TileGeom kTileGeom[kNumTiles] = {
+    {256, 256, 64, 2, 256, 8},
+    {128, 128, 64, 2, 256, 8},
+};
+
+// (vec_a, vec_b) pairs with a compiled instance, in order of preference.
+constexpr int kNumVecPairs = 6;
+constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 2}, {1, 1}};
+
+struct DtypeKernels {
+    const void* tiled[kNumTiles][kNumVecPairs];
+    const void* direct;
+};
+
+const DtypeKernels& kernels_f16();
+const DtypeKernels& kernels_bf16();
+const void* zero_fill_kernel();
+
+}  // namespace gemm_relu_hip

@@ -1,0 +1,45 @@
+// Instances of the gfx950 GEMM + ReLU kernels for the bf16 dtype.
+#include "gemm_relu_kernels.hpp"
+#include "kernel_table.hpp"
+
+namespace gemm_relu_hip {
+
+namespace {
+using Tile256 = TileConfig<256, 256, 2, 2, 8>;
+using Tile128 = TileConfig<128, 128, 2, 2, 8>;
+
+template <class Cfg, int id>
+constexpr bool geom_matches = Cfg::BM == kTileGeom[id].bm && Cfg::BN == kTileGeom[id].bn &&
+                              Cfg::BK == kTileGeom[id].bk && Cfg::STAGES == kTileGeom[id].stages &&
+                              Cfg::THREADS == kTileGeom[id].threads && Cfg::GROUP_M == kTileGeom[id].group_m;
+static_assert(geom_matches<Tile256, kTile256> && geom_matches<Tile128, kTile128>,
+              "host tile table out of date");
+
+template <class Cfg>
+void fill_row(const void** row)
+{
+    row[0] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 8, 8>;
+    row[1] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 4, 8>;
+    row[2] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 8, 4>;
+    row[3] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 4, 4>;
+    row[4] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 2, 2>;
+    row[5] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 1, 1>;
+}
+
+DtypeKernels make_table()
+{
+    DtypeKernels t;
+    fill_row<Tile256>(t.tiled[kTile256]);
+    fill_row<Tile128>(t.tiled[kTile128]);
+    t.direct = (const void*)&gemm_relu_direct<kBF16>;
+    return t;
+}
+}  // namespace
+
+const DtypeKernels& kernels_bf16()
+{
+    static const DtypeKernels table = make_table();
+    return table;
+}
+
+}  // namespace gemm_relu_hip
