@@ -106,6 +106,23 @@ def cpu_baseline(w, target_s):
             "seconds": dt}
 
 
+def copy_calibration(device, n_bytes=1 << 30, reps=5):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch give the
+    factor between those counters and true HBM bytes."""
+    src = torch.ones(n_bytes // 2, dtype=torch.float16, device=device)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(device)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize(device)
+    ms = t0.elapsed_time(t1) / reps
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "reps": reps,
+                      "ms": round(ms, 4), "GB/s": round(2 * n_bytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
@@ -117,6 +134,8 @@ def main():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = p.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -128,6 +147,9 @@ def main():
         sys.exit(1)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.copy_calibration:
+        copy_calibration(device)
+        return
     gr.load_library()
 
     w = inputs.WORKLOADS[args.workload]

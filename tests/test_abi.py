@@ -73,7 +73,7 @@ def test_invalid_arguments_are_rejected_before_launch(lib, args, code):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 3, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 4, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -90,8 +90,8 @@ def test_k_zero_needs_no_inputs():
 
 def test_config_choice_for_the_workload_shapes():
     big = gr.selected_config(8192, 8192, 8192)
-    assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (1, 256, 256, 64)
-    assert (big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (8, 8, 1024, 131072)
+    assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (3, 256, 256, 32)
+    assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (4, 8, 8, 1024, 131072)
     small = gr.selected_config(1024, 1024, 1024)
     assert (small["config_id"], small["block_m"], small["grid"]) == (2, 128, 64)
     ragged = gr.selected_config(4000, 11000, 4100)
@@ -108,6 +108,13 @@ def test_config_choice_for_the_workload_shapes():
 def test_load_width_follows_row_length_and_alignment(K, N, a_off, b_off, want):
     cfg = gr.selected_config(512, N, K, config=1, a_ptr=4096 + a_off, b_ptr=(1 << 20) + b_off)
     assert (cfg["vec_a"], cfg["vec_b"]) == want
+
+
+def test_dma_config_falls_back_without_16_byte_loads():
+    assert gr.selected_config(512, 512, 512, config=3)["config_id"] == 3
+    cfg = gr.selected_config(512, 512, 516, config=3)            # K % 8 != 0
+    assert (cfg["config_id"], cfg["vec_a"]) == (1, 4)
+    assert gr.selected_config(512, 512, 512, config=3, a_ptr=4096 + 8)["config_id"] == 1
 
 
 def test_direct_config_geometry():

@@ -17,8 +17,9 @@ CONFIG_AUTO = -1
 CONFIG_DIRECT = 0
 CONFIG_TILE_256 = 1
 CONFIG_TILE_128 = 2
+CONFIG_DMA_256 = 3
 CONFIG_NAMES = {CONFIG_DIRECT: "direct_32x32", CONFIG_TILE_256: "tile_256x256x64",
-                CONFIG_TILE_128: "tile_128x128x64"}
+                CONFIG_TILE_128: "tile_128x128x64", CONFIG_DMA_256: "dma_256x256x32_4stage"}
 
 ERRORS = {
     0: "OK", -1: "INVALID_ARG", -2: "BAD_DTYPE", -3: "ALIAS", -4: "MISALIGNED", -5: "NO_DEVICE",

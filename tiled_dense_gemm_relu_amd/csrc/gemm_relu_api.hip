@@ -20,7 +20,7 @@ constexpr int kDirectTile = 32;
 
 struct Plan {
     gemm_relu_config_t cfg;
-    int tile;          // TileId, or -1 for the direct kernel, -2 for the K == 0 fill
+    int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 LDS-DMA 256 kernel
     int vec_pair;      // index into kVecPairs
     int tiles_m, tiles_n;
     int c_vec_ok;
@@ -51,7 +51,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 {
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
-    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_TILE_128)
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_256)
         return GEMM_RELU_ERR_BAD_CONFIG;
     if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
 
@@ -82,14 +82,41 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         return GEMM_RELU_OK;
     }
 
+    const int va = vec_width(A, K), vb = vec_width(B, N);
+    const bool full_vectors = va == 8 && vb == 8;
     int chosen = config_id;
     if (chosen == GEMM_RELU_CONFIG_AUTO) {
-        // The 256x256 tile when it yields enough workgroups to cover the 256
-        // CUs a few times over; otherwise the 128x128 tile (4x the workgroups).
+        // 256x256 tiles when they yield enough workgroups to cover the 256 CUs
+        // a few times over (the LDS-DMA kernel when 16-byte loads are possible);
+        // otherwise the 128x128 tile (4x the workgroups).
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-        chosen = t256 >= 192 ? GEMM_RELU_CONFIG_TILE_256 : GEMM_RELU_CONFIG_TILE_128;
+        if (t256 >= 192)
+            chosen = full_vectors ? GEMM_RELU_CONFIG_DMA_256 : GEMM_RELU_CONFIG_TILE_256;
+        else
+            chosen = GEMM_RELU_CONFIG_TILE_128;
     }
+    if (chosen == GEMM_RELU_CONFIG_DMA_256 && !full_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     plan->cfg.config_id = chosen;
+
+    if (chosen == GEMM_RELU_CONFIG_DMA_256) {
+        const TileGeom& g = kDma256Geom;
+        if (int64_t(g.bm) * K * 2 > kMaxBand || int64_t(g.bk) * N * 2 > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
+        const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
+        if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
+        plan->tile = -4;
+        plan->tiles_m = (int)tm;
+        plan->tiles_n = (int)tn;
+        plan->cfg.block_m = g.bm;
+        plan->cfg.block_n = g.bn;
+        plan->cfg.block_k = g.bk;
+        plan->cfg.stages = g.stages;
+        plan->cfg.threads = g.threads;
+        plan->cfg.vec_a = 8;
+        plan->cfg.vec_b = 8;
+        plan->cfg.grid = tm * tn;
+        plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2;
+        return GEMM_RELU_OK;
+    }
 
     if (chosen == GEMM_RELU_CONFIG_DIRECT) {
         const int64_t tm = ceil_div(M, kDirectTile), tn = ceil_div(N, kDirectTile);
@@ -114,7 +141,6 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
     if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
 
-    const int va = vec_width(A, K), vb = vec_width(B, N);
     int pair = kNumVecPairs - 1;
     for (int i = 0; i < kNumVecPairs; ++i)
         if (kVecPairs[i][0] <= va && kVecPairs[i][1] <= vb) { pair = i; break; }
@@ -170,8 +196,8 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
     } else {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
-        err = hipLaunchKernel(ks.tiled[p.tile][p.vec_pair], dim3((unsigned)p.cfg.grid),
-                              dim3((unsigned)p.cfg.threads), args, 0, stream);
+        const void* fn = p.tile == -4 ? ks.dma256 : ks.tiled[p.tile][p.vec_pair];
+        err = hipLaunchKernel(fn, dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     }
     return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;
 }

@@ -352,6 +352,231 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
                             M, N, c_vec_ok != 0);
 }
 
+// ---------------------------------------------------------------- LDS-DMA kernel
+
+// 256x256x32 block tile, 4 waves (2x2, each 128x128), a ring of 4 LDS stages
+// filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): tile
+// data goes from L2 into LDS without passing through VGPRs, so loads run three
+// K-steps ahead of the MFMAs at no register cost.  This is the pages'
+// multi-stage software pipeline (T.Pipelined with several stages in flight),
+// built from gfx950 LDS DMA instead of cp.async/TMA.
+//
+// LDS layout of one stage (32 KB):
+//  * A tile, 256 rows (m) x 32 k, 64 bytes per row: chunk c (8 k values) of
+//    row r at 16 * (c ^ ((r >> 2) & 3)).  Sixteen lanes reading 16 consecutive
+//    rows at one logical chunk (one ds_read_b128) hit 16 distinct 16-byte bank
+//    groups.
+//  * B tile, 32 rows (k) x 256 n, 512 bytes per row, kept N-contiguous as it is
+//    in memory: chunk c (8 n values) of row k at 16 * (c ^ (4 * (k & 3))).
+//    MFMA operands need 8 consecutive k per lane; ds_read_b64_tr_b16 gives
+//    them: within each group of 16 lanes, source lane s points at row s / 4,
+//    columns 4 (s % 4) .. +3 of a 4 x 16 block, and lane j receives the 4 k
+//    values of column j.  The swizzle puts the 4 rows x 64 bytes that 32 lanes
+//    read at once in 16 distinct bank groups.
+// A DMA instruction writes 1 KB of LDS at consecutive 16-byte slots (lane l at
+// base + 16 l); the swizzle is applied by choosing which global chunk lane l
+// fetches.
+//
+// Synchronisation: the DMA loads are issued from inline assembly, so the
+// compiler does not add its own (maximal) waits before LDS reads; the kernel
+// waits for exactly the loads of the stage it is about to read
+// (s_waitcnt vmcnt) and then meets the other waves at one s_barrier per K-step.
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor as four dwords (base, stride 0, num_records, flags).
+__device__ __forceinline__ int32x4_t rsrc_words(const void* base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return int32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kBufferFlags};
+}
+
+// 64 lanes x 16 bytes from the buffer into LDS [lds_addr, lds_addr + 1024).
+__device__ __forceinline__ void dma_b128(int32x4_t rsrc, uint32_t lds_addr, uint32_t voffset)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// All of this wave's LDS reads are complete, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint8_t* p)
+{
+    short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+struct DmaTile256 {
+    static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, THREADS = 256, GROUP_M = 8;
+    static constexpr int A_BYTES = BM * BK * 2;          // 16 KB
+    static constexpr int B_BYTES = BK * BN * 2;          // 16 KB
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int LOADS_PER_STAGE = 8;            // per wave: 4 A + 4 B DMA instructions
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+template <int DT>
+__global__ __launch_bounds__(256, 1) void gemm_relu_dma256(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok)
+{
+    using Cfg = DmaTile256;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int KT = (K + BK - 1) / BK;
+
+    // A: rows m0 .. m0 + valid_m - 1 of A; rows past M read as zero.
+    const int valid_m = min(BM, M - m0);
+    const int32x4_t rsrc_a = rsrc_words(A + (size_t)m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+
+    // DMA source offsets.  Wave w fills A rows [64w, 64w + 64) (4 instructions
+    // of 16 rows) and B rows [8w, 8w + 8) (4 instructions of 2 rows).
+    uint32_t a_row_off[4];
+    int a_kcol[4];
+    uint32_t b_off[4];
+    bool b_col_ok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = (wave * 4 + q) * 16 + (lane >> 2);
+        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+        a_row_off[q] = (uint32_t)row * (uint32_t)K * 2u;
+        a_kcol[q] = lc * 8;
+        const int brow = (wave * 4 + q) * 2 + (lane >> 5);
+        const int blc = (lane & 31) ^ (4 * (brow & 3));
+        b_off[q] = (uint32_t)brow * (uint32_t)N * 2u + (uint32_t)(n0 + blc * 8) * 2u;
+        b_col_ok[q] = n0 + blc * 8 < N;
+    }
+
+    auto issue = [&](int kt) {
+        const uint32_t st = lds_base + (uint32_t)((kt % S) * Cfg::STAGE_BYTES);
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kc = k0 + a_kcol[q];
+            dma_b128(rsrc_a, st + (wave * 4 + q) * 1024,
+                     kc < K ? a_row_off[q] + (uint32_t)kc * 2u : kOobOffset);
+        }
+        const int valid_k = min(BK, K - k0);
+        const int32x4_t rsrc_b = rsrc_words(B + (size_t)k0 * (size_t)N, (uint32_t)valid_k * (uint32_t)N * 2u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dma_b128(rsrc_b, st + Cfg::A_BYTES + (wave * 4 + q) * 1024, b_col_ok[q] ? b_off[q] : kOobOffset);
+    };
+
+    // Per-lane LDS read offsets inside a stage.
+    //  A fragment j, k-half ks: row wm*128 + 32j + lane%32, chunk 2ks + lane/32.
+    uint32_t a_frag_off[2];
+    {
+        const int row = wm * 128 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            a_frag_off[ks] = (uint32_t)(row * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)));
+    }
+    //  B^T fragment i, k-half ks, half hh: lane group g = lane/16, j = lane%16;
+    //  row k = 16ks + 8(g/2) + 4hh + j/4, column n = wn*128 + 32i + 16(g%2) + 4(j%4).
+    uint32_t b_frag_off[4];
+    {
+        const int g = lane >> 4, j = lane & 15;
+        const int krow = 8 * (g >> 1) + (j >> 2);          // + 16ks + 4hh, which keep k & 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = wn * 128 + i * 32 + 16 * (g & 1) + 4 * (j & 3);
+            b_frag_off[i] = (uint32_t)(Cfg::A_BYTES + krow * 512 + 16 * ((n >> 3) ^ (4 * (krow & 3))) +
+                                       8 * (j & 1));
+        }
+    }
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
+
+    u32x4 fa[2][4], fb[2][4];   // [buffer][fragment]: B^T fragments (MFMA A operand) and A fragments
+    auto read_frags = [&](int buf, const uint8_t* st, int ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fb[buf][j] = *reinterpret_cast<const u32x4*>(st + a_frag_off[ks] + j * 32 * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x2 lo = ds_read_tr16(st + b_frag_off[i] + (16 * ks + 0) * 512);
+            const u32x2 hi = ds_read_tr16(st + b_frag_off[i] + (16 * ks + 4) * 512);
+            fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<DT>(fa[buf][i], fb[buf][j], acc[i][j]);
+    };
+    // Wait until the loads of stage kt have landed (this wave's), given how many
+    // later stages this wave has already issued, then meet the other waves.
+    auto wait_stage = [&](int kt) {
+        const int later = min(S - 2, KT - 1 - kt);
+        if (later >= 2) wait_vmcnt<2 * Cfg::LOADS_PER_STAGE>();
+        else if (later == 1) wait_vmcnt<Cfg::LOADS_PER_STAGE>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+    };
+
+    if (KT > 0) {
+        // Prologue: stages 0 .. S-2 in flight, then stage 0's first fragments.
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s)
+            if (s < KT) issue(s);
+        wait_stage(0);
+        read_frags(0, smem, 0);
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+        const uint8_t* st = smem + (kt % S) * Cfg::STAGE_BYTES;
+        // Stage kt+3 goes into the buffer of stage kt-1, which every wave
+        // finished reading before the last barrier.
+        if (kt + S - 1 < KT) issue(kt + S - 1);
+        // First k-half of stage kt; meanwhile read its second k-half.
+        read_frags(1, st, 1);
+        mfmas(0);
+        // Second k-half; meanwhile wait for stage kt+1 and read its first k-half.
+        if (kt + 1 < KT) {
+            wait_stage(kt + 1);
+            read_frags(0, smem + ((kt + 1) % S) * Cfg::STAGE_BYTES, 0);
+        }
+        mfmas(1);
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            store_block<DT>(C, acc[i][j], lane, m0 + wm * 128 + j * 32, n0 + wn * 128 + i * 32, M, N,
+                            c_vec_ok != 0);
+}
+
 // ---------------------------------------------------------------- direct kernel
 
 // One wave per 32x32 block of C, operands gathered straight from global memory

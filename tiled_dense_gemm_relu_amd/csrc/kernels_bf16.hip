@@ -14,6 +14,10 @@ constexpr bool geom_matches = Cfg::BM == kTileGeom[id].bm && Cfg::BN == kTileGeo
                               Cfg::THREADS == kTileGeom[id].threads && Cfg::GROUP_M == kTileGeom[id].group_m;
 static_assert(geom_matches<Tile256, kTile256> && geom_matches<Tile128, kTile128>,
               "host tile table out of date");
+static_assert(DmaTile256::BM == kDma256Geom.bm && DmaTile256::BN == kDma256Geom.bn &&
+                  DmaTile256::BK == kDma256Geom.bk && DmaTile256::STAGES == kDma256Geom.stages &&
+                  DmaTile256::THREADS == kDma256Geom.threads && DmaTile256::GROUP_M == kDma256Geom.group_m,
+              "host DMA tile geometry out of date");
 
 template <class Cfg>
 void fill_row(const void** row)
@@ -32,6 +36,7 @@ DtypeKernels make_table()
     fill_row<Tile256>(t.tiled[kTile256]);
     fill_row<Tile128>(t.tiled[kTile128]);
     t.direct = (const void*)&gemm_relu_direct<kBF16>;
+    t.dma256 = (const void*)&gemm_relu_dma256<kBF16>;
     return t;
 }
 }  // namespace
