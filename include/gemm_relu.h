@@ -67,7 +67,7 @@ enum {
     GEMM_RELU_CONFIG_DIRECT = 0,      /* one wave per 32x32 block, operands from global memory */
     GEMM_RELU_CONFIG_TILE_256 = 1,    /* 256x256x64 block tile, 4 waves, 2 LDS stages */
     GEMM_RELU_CONFIG_TILE_128 = 2,    /* 128x128x64 block tile, 4 waves, 2 LDS stages */
-    GEMM_RELU_CONFIG_DMA_256 = 3      /* 256x256x32 block tile, 4 waves, 4 LDS stages filled by
+    GEMM_RELU_CONFIG_DMA_256 = 3      /* 256x256x32 block tile, 8 waves, 4 LDS stages filled by
                                          direct-to-LDS loads; used when A and B allow 16-byte
                                          loads (K % 8 == 0, N % 8 == 0, 16-byte aligned A and B),
                                          otherwise the request falls back to GEMM_RELU_CONFIG_TILE_256 */

@@ -66,7 +66,10 @@ def assert_within_tolerance(got_bits, want_bits, dtype):
 # ------------------------------------------------------------- integer inputs
 
 INT_SHAPES = [(1, 1, 1), (32, 32, 16), (33, 65, 17), (255, 257, 63), (257, 255, 65),
-              (300, 520, 130), (129, 131, 200), (512, 256, 192), (64, 1000, 1024)]
+              (300, 520, 130), (129, 131, 200), (512, 256, 192), (64, 1000, 1024),
+              # 16-byte-loadable shapes for the LDS-DMA kernel: a K tail (K % 32 != 0),
+              # fewer K-steps than pipeline stages, and M / N tails
+              (300, 520, 200), (256, 256, 40), (64, 64, 8), (257, 264, 96), (520, 776, 1064)]
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])

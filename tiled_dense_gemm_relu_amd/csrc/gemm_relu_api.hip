@@ -196,7 +196,7 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
     } else {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
-        const void* fn = p.tile == -4 ? ks.dma256 : ks.tiled[p.tile][p.vec_pair];
+        const void* fn = p.tile == -4 ? ks.dma256[K % kDma256Geom.bk != 0 ? 1 : 0] : ks.tiled[p.tile][p.vec_pair];
         err = hipLaunchKernel(fn, dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     }
     return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;

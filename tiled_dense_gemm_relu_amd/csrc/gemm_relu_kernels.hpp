@@ -354,20 +354,23 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 
 // ---------------------------------------------------------------- LDS-DMA kernel
 
-// 256x256x32 block tile, 4 waves (2x2, each 128x128), a ring of 4 LDS stages
-// filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): tile
-// data goes from L2 into LDS without passing through VGPRs, so loads run three
-// K-steps ahead of the MFMAs at no register cost.  This is the pages'
-// multi-stage software pipeline (T.Pipelined with several stages in flight),
-// built from gfx950 LDS DMA instead of cp.async/TMA.
+// 256x256x32 block tile, 8 waves (4 along m x 2 along n, each 64x128), a ring
+// of 4 LDS stages filled by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds): tile data goes from L2 into LDS without
+// passing through VGPRs, so loads run three K-steps ahead of the MFMAs at no
+// register cost.  This is the pages' multi-stage software pipeline
+// (T.Pipelined with several stages in flight), built from gfx950 LDS DMA
+// instead of cp.async/TMA.  Two waves share each SIMD, so one wave's LDS and
+// barrier waits are covered by the other's MFMAs.
 //
-// LDS layout of one stage (32 KB):
-//  * A tile, 256 rows (m) x 32 k, 64 bytes per row: chunk c (8 k values) of
+// LDS layout (128 KB): A stages at [0, 64K), B stages at [64K, 128K), 16 KB
+// each, so every per-stage offset fits a ds_read immediate.
+//  * A stage, 256 rows (m) x 32 k, 64 bytes per row: chunk c (8 k values) of
 //    row r at 16 * (c ^ ((r >> 2) & 3)).  Sixteen lanes reading 16 consecutive
 //    rows at one logical chunk (one ds_read_b128) hit 16 distinct 16-byte bank
-//    groups.
-//  * B tile, 32 rows (k) x 256 n, 512 bytes per row, kept N-contiguous as it is
-//    in memory: chunk c (8 n values) of row k at 16 * (c ^ (4 * (k & 3))).
+//    groups; the swizzle is unchanged by adding a multiple of 16 rows.
+//  * B stage, 32 rows (k) x 256 n, 512 bytes per row, kept N-contiguous as it
+//    is in memory: chunk c (8 n values) of row k at 16 * (c ^ (4 * (k & 3))).
 //    MFMA operands need 8 consecutive k per lane; ds_read_b64_tr_b16 gives
 //    them: within each group of 16 lanes, source lane s points at row s / 4,
 //    columns 4 (s % 4) .. +3 of a 4 x 16 block, and lane j receives the 4 k
@@ -377,10 +380,17 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 // base + 16 l); the swizzle is applied by choosing which global chunk lane l
 // fetches.
 //
+// One K-step: MFMAs on the k-half already in registers, interleaved (one
+// instruction group per MFMA) with the DMA of stage kt+3 and the reads of the
+// second k-half; then wait for stage kt+1 and meet the other waves at the
+// barrier; then MFMAs on the second k-half interleaved with the reads of stage
+// kt+1's first k-half.  The loop body has no branches: stages past the end are
+// "loaded" through a zero-length buffer descriptor (nothing is fetched).
+//
 // Synchronisation: the DMA loads are issued from inline assembly, so the
 // compiler does not add its own (maximal) waits before LDS reads; the kernel
 // waits for exactly the loads of the stage it is about to read
-// (s_waitcnt vmcnt) and then meets the other waves at one s_barrier per K-step.
+// (s_waitcnt vmcnt) before the barrier.
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
@@ -393,11 +403,12 @@ __device__ __forceinline__ int32x4_t rsrc_words(const void* base, uint32_t bytes
 }
 
 // 64 lanes x 16 bytes from the buffer into LDS [lds_addr, lds_addr + 1024).
-__device__ __forceinline__ void dma_b128(int32x4_t rsrc, uint32_t lds_addr, uint32_t voffset)
+// voffset is per lane, soffset is uniform.
+__device__ __forceinline__ void dma_b128(int32x4_t rsrc, uint32_t lds_addr, uint32_t voffset, uint32_t soffset)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
                  : "memory", "m0");
 }
 
@@ -422,27 +433,35 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint8_t* p)
 }
 
 struct DmaTile256 {
-    static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, THREADS = 256, GROUP_M = 8;
-    static constexpr int A_BYTES = BM * BK * 2;          // 16 KB
-    static constexpr int B_BYTES = BK * BN * 2;          // 16 KB
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int LOADS_PER_STAGE = 8;            // per wave: 4 A + 4 B DMA instructions
+    static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, GROUP_M = 4;
+    static constexpr int WAVES_M = 4, WAVES_N = 2, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;     // 64 x 128 per wave
+    static constexpr int FM = WTM / 32, FN = WTN / 32;               // 32x32 MFMA blocks per wave
+    static constexpr int STAGE_BYTES = 16384;                        // one operand, one stage
+    static constexpr int B_REGION = STAGES * STAGE_BYTES;            // B stages after the A stages
+    static constexpr int LDS_BYTES = 2 * STAGES * STAGE_BYTES;
+    static constexpr int QD = 16 / WAVES;                            // DMA instructions per wave per operand per stage
+    static constexpr int LOADS_PER_STAGE = 2 * QD;                   // per wave
+    static_assert(BM * BK * 2 == STAGE_BYTES && BK * BN * 2 == STAGE_BYTES, "stage sizes");
+    static_assert(QD * WAVES == 16, "16 DMA instructions of 1 KB fill one operand stage");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int DT>
-__global__ __launch_bounds__(256, 1) void gemm_relu_dma256(
+// KTAIL: K is not a multiple of 32, so the last stage is partial and its A
+// chunks past K are masked (K % 8 == 0 is still required).
+template <int DT, bool KTAIL>
+__global__ __launch_bounds__(DmaTile256::THREADS, 1) void gemm_relu_dma256(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok)
 {
     using Cfg = DmaTile256;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES, STAGE = Cfg::STAGE_BYTES;
+    constexpr int QD = Cfg::QD, FM = Cfg::FM, FN = Cfg::FN, WTM = Cfg::WTM, WTN = Cfg::WTN;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
@@ -452,128 +471,132 @@ __global__ __launch_bounds__(256, 1) void gemm_relu_dma256(
     // A: rows m0 .. m0 + valid_m - 1 of A; rows past M read as zero.
     const int valid_m = min(BM, M - m0);
     const int32x4_t rsrc_a = rsrc_words(A + (size_t)m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+    const int32x4_t rsrc_none = rsrc_words(A, 0u);
+    const uint32_t lds_wave =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + (uint32_t)(wave * QD * 1024);
 
-    // DMA source offsets.  Wave w fills A rows [64w, 64w + 64) (4 instructions
-    // of 16 rows) and B rows [8w, 8w + 8) (4 instructions of 2 rows).
-    uint32_t a_row_off[4];
-    int a_kcol[4];
-    uint32_t b_off[4];
-    bool b_col_ok[4];
+    // DMA source offsets: wave w fills A rows [16 QD w, 16 QD (w+1)) and B
+    // rows [2 QD w, 2 QD (w+1)) of every stage.
+    uint32_t a_voff[QD], b_voff[QD];
+    int a_kcol[QD];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int row = (wave * 4 + q) * 16 + (lane >> 2);
+    for (int q = 0; q < QD; ++q) {
+        const int row = (wave * QD + q) * 16 + (lane >> 2);
         const int lc = (lane & 3) ^ ((row >> 2) & 3);
-        a_row_off[q] = (uint32_t)row * (uint32_t)K * 2u;
+        a_voff[q] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)lc * 16u;
         a_kcol[q] = lc * 8;
-        const int brow = (wave * 4 + q) * 2 + (lane >> 5);
+        const int brow = (wave * QD + q) * 2 + (lane >> 5);
         const int blc = (lane & 31) ^ (4 * (brow & 3));
-        b_off[q] = (uint32_t)brow * (uint32_t)N * 2u + (uint32_t)(n0 + blc * 8) * 2u;
-        b_col_ok[q] = n0 + blc * 8 < N;
+        b_voff[q] = n0 + blc * 8 < N ? (uint32_t)brow * (uint32_t)N * 2u + (uint32_t)(n0 + blc * 8) * 2u
+                                     : kOobOffset;
     }
+    const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
 
-    auto issue = [&](int kt) {
-        const uint32_t st = lds_base + (uint32_t)((kt % S) * Cfg::STAGE_BYTES);
+    // DMA q (0 .. QD-1: A, QD .. 2QD-1: B) of stage kt into ring slot st.
+    auto dma = [&](int kt, uint32_t st, int q) {
         const int k0 = kt * BK;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int kc = k0 + a_kcol[q];
-            dma_b128(rsrc_a, st + (wave * 4 + q) * 1024,
-                     kc < K ? a_row_off[q] + (uint32_t)kc * 2u : kOobOffset);
+        const bool live = kt < KT;
+        if (q < QD) {
+            uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
+            if (KTAIL) {   // chunks past K read as zero
+                vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
+                so = 0u;
+            }
+            dma_b128(live ? rsrc_a : rsrc_none, lds_wave + st + q * 1024, vo, live ? so : 0u);
+        } else {
+            const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
+            const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N, nb) : rsrc_none;
+            dma_b128(rb, lds_wave + Cfg::B_REGION + st + (q - QD) * 1024, b_voff[q - QD], 0u);
         }
-        const int valid_k = min(BK, K - k0);
-        const int32x4_t rsrc_b = rsrc_words(B + (size_t)k0 * (size_t)N, (uint32_t)valid_k * (uint32_t)N * 2u);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dma_b128(rsrc_b, st + Cfg::A_BYTES + (wave * 4 + q) * 1024, b_col_ok[q] ? b_off[q] : kOobOffset);
     };
 
     // Per-lane LDS read offsets inside a stage.
-    //  A fragment j, k-half ks: row wm*128 + 32j + lane%32, chunk 2ks + lane/32.
+    //  A fragment j, k-half ks: row wm*WTM + 32j + lane%32, chunk 2ks + lane/32.
     uint32_t a_frag_off[2];
     {
-        const int row = wm * 128 + (lane & 31);
+        const int row = wm * WTM + (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             a_frag_off[ks] = (uint32_t)(row * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)));
     }
     //  B^T fragment i, k-half ks, half hh: lane group g = lane/16, j = lane%16;
-    //  row k = 16ks + 8(g/2) + 4hh + j/4, column n = wn*128 + 32i + 16(g%2) + 4(j%4).
-    uint32_t b_frag_off[4];
+    //  row k = 16ks + 8(g/2) + 4hh + j/4, column n = wn*WTN + 32i + 16(g%2) + 4(j%4).
+    uint32_t b_frag_off[FN];
     {
         const int g = lane >> 4, j = lane & 15;
         const int krow = 8 * (g >> 1) + (j >> 2);          // + 16ks + 4hh, which keep k & 3
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = wn * 128 + i * 32 + 16 * (g & 1) + 4 * (j & 3);
-            b_frag_off[i] = (uint32_t)(Cfg::A_BYTES + krow * 512 + 16 * ((n >> 3) ^ (4 * (krow & 3))) +
-                                       8 * (j & 1));
+        for (int i = 0; i < FN; ++i) {
+            const int n = wn * WTN + i * 32 + 16 * (g & 1) + 4 * (j & 3);
+            b_frag_off[i] = (uint32_t)(Cfg::B_REGION + krow * 512 + 16 * ((n >> 3) ^ (4 * (krow & 3))) + 8 * (j & 1));
         }
     }
 
-    floatx16 acc[4][4];
+    floatx16 acc[FN][FM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
+        for (int j = 0; j < FM; ++j) acc[i][j] = floatx16{0};
 
-    u32x4 fa[2][4], fb[2][4];   // [buffer][fragment]: B^T fragments (MFMA A operand) and A fragments
-    auto read_frags = [&](int buf, const uint8_t* st, int ks) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            fb[buf][j] = *reinterpret_cast<const u32x4*>(st + a_frag_off[ks] + j * 32 * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x2 lo = ds_read_tr16(st + b_frag_off[i] + (16 * ks + 0) * 512);
-            const u32x2 hi = ds_read_tr16(st + b_frag_off[i] + (16 * ks + 4) * 512);
-            fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+    // [k-half][fragment]: B^T fragments (MFMA A operand) and A fragments (MFMA B operand)
+    u32x4 fa[2][FN], fb[2][FM];
+    auto read_a = [&](int buf, uint32_t st, int ks, int j) {
+        fb[buf][j] = *reinterpret_cast<const u32x4*>(smem + st + a_frag_off[ks] + j * 32 * 64);
     };
-    auto mfmas = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<DT>(fa[buf][i], fb[buf][j], acc[i][j]);
+    auto read_b = [&](int buf, uint32_t st, int ks, int i) {
+        const u32x2 lo = ds_read_tr16(smem + st + b_frag_off[i] + (16 * ks + 0) * 512);
+        const u32x2 hi = ds_read_tr16(smem + st + b_frag_off[i] + (16 * ks + 4) * 512);
+        fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
     };
-    // Wait until the loads of stage kt have landed (this wave's), given how many
-    // later stages this wave has already issued, then meet the other waves.
-    auto wait_stage = [&](int kt) {
-        const int later = min(S - 2, KT - 1 - kt);
-        if (later >= 2) wait_vmcnt<2 * Cfg::LOADS_PER_STAGE>();
-        else if (later == 1) wait_vmcnt<Cfg::LOADS_PER_STAGE>();
-        else wait_vmcnt<0>();
-        lds_barrier();
+    auto mfma1 = [&](int buf, int t) {
+        const int i = t / FM, j = t % FM;
+        acc[i][j] = mfma_32x32x16<DT>(fa[buf][i], fb[buf][j], acc[i][j]);
     };
+    constexpr int NQ = Cfg::LOADS_PER_STAGE, NF = FM + FN, NMF = FM * FN;
+    static_assert(NQ <= NMF && NF <= NMF, "one DMA and one fragment read per MFMA slot");
 
-    if (KT > 0) {
-        // Prologue: stages 0 .. S-2 in flight, then stage 0's first fragments.
+    // Prologue: stages 0..2 in flight, stage 0 landed, its first k-half read.
 #pragma unroll
-        for (int s = 0; s < S - 1; ++s)
-            if (s < KT) issue(s);
-        wait_stage(0);
-        read_frags(0, smem, 0);
-    }
+    for (int s = 0; s < S - 1; ++s)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) dma(s, s * STAGE, q);
+    wait_vmcnt<(S - 2) * NQ>();
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < FM; ++j) read_a(0, 0, 0, j);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) read_b(0, 0, 0, i);
+
     for (int kt = 0; kt < KT; ++kt) {
-        const uint8_t* st = smem + (kt % S) * Cfg::STAGE_BYTES;
-        // Stage kt+3 goes into the buffer of stage kt-1, which every wave
-        // finished reading before the last barrier.
-        if (kt + S - 1 < KT) issue(kt + S - 1);
-        // First k-half of stage kt; meanwhile read its second k-half.
-        read_frags(1, st, 1);
-        mfmas(0);
-        // Second k-half; meanwhile wait for stage kt+1 and read its first k-half.
-        if (kt + 1 < KT) {
-            wait_stage(kt + 1);
-            read_frags(0, smem + ((kt + 1) % S) * Cfg::STAGE_BYTES, 0);
+        const uint32_t st = (uint32_t)(kt & (S - 1)) * STAGE;
+        const uint32_t stn = (uint32_t)((kt + 1) & (S - 1)) * STAGE;
+        const uint32_t sti = (uint32_t)((kt + S - 1) & (S - 1)) * STAGE;   // slot of stage kt-1, free since the last barrier
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+            mfma1(0, t);
+            if (t < NQ) dma(kt + S - 1, sti, t);
+            if (t < FM) read_a(1, st, 1, t);
+            else if (t < NF) read_b(1, st, 1, t - FM);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        mfmas(1);
+        wait_vmcnt<(S - 2) * NQ>();        // stage kt+1 landed (for this wave)
+        lds_barrier();                     // ... and for every wave
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+            mfma1(1, t);
+            if (t < FM) read_a(0, stn, 0, t);
+            else if (t < NF) read_b(0, stn, 0, t - FM);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
 
+    // Fused epilogue: ReLU, round to the dtype, masked store.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            store_block<DT>(C, acc[i][j], lane, m0 + wm * 128 + j * 32, n0 + wn * 128 + i * 32, M, N,
+        for (int j = 0; j < FM; ++j)
+            store_block<DT>(C, acc[i][j], lane, m0 + wm * WTM + j * 32, n0 + wn * WTN + i * 32, M, N,
                             c_vec_ok != 0);
 }
 

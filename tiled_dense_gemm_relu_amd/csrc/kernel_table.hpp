@@ -24,11 +24,11 @@ constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 
 struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
     const void* direct;
-    const void* dma256;   // 256x256x32, 4 LDS-DMA stages; needs 8-element loads of A and B
+    const void* dma256[2];   // 256x256x32, 4 LDS-DMA stages; [K % 32 != 0]; needs 8-element loads of A and B
 };
 
 // Geometry of the LDS-DMA kernel (must match DmaTile256).
-constexpr TileGeom kDma256Geom = {256, 256, 32, 4, 256, 8};
+constexpr TileGeom kDma256Geom = {256, 256, 32, 4, 512, 4};
 
 const DtypeKernels& kernels_f16();
 const DtypeKernels& kernels_bf16();

@@ -36,7 +36,8 @@ DtypeKernels make_table()
     fill_row<Tile256>(t.tiled[kTile256]);
     fill_row<Tile128>(t.tiled[kTile128]);
     t.direct = (const void*)&gemm_relu_direct<kF16>;
-    t.dma256 = (const void*)&gemm_relu_dma256<kF16>;
+    t.dma256[0] = (const void*)&gemm_relu_dma256<kF16, false>;
+    t.dma256[1] = (const void*)&gemm_relu_dma256<kF16, true>;
     return t;
 }
 }  // namespace
