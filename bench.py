@@ -33,6 +33,26 @@ PEAK_HBM_GBS = 8000.0                               # MI355X HBM3E, published
 METRIC = "TFLOP/s and % of MI355X dense fp16 MFMA peak, ReLU(A@B) 8192³"
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "dma256_square_8192_fp16_traffic.json")
+
+
+def measured_traffic(workload_name, kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by the
+    copy-kernel calibration; None unless they were taken on this workload, this kernel and the
+    current kernel sources."""
+    from tiled_dense_gemm_relu_amd.build import kernel_source_digest
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if not prof.get("workload", "").startswith(workload_name) or kernel_name != "dma_256x256x32_4stage":
+        return None
+    if prof.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return int(prof["traffic_bytes_per_launch"])
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -201,7 +221,8 @@ def main():
                    "grid": cfg["grid"], "rotated_sets": args.sets},
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(kernel_tflops / peak, 4), "traffic": None},
+                     "frac": round(kernel_tflops / peak, 4),
+                     "traffic": measured_traffic(w.name, binding.CONFIG_NAMES.get(cfg["config_id"]))},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

@@ -35,6 +35,19 @@ HIPCC_FLAGS = [
 ]
 
 
+KERNEL_SOURCES = ["gemm_relu_kernels.hpp", "kernels_f16.hip", "kernels_bf16.hip"]
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the kernel sources: identifies the kernels a profile was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
