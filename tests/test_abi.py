@@ -73,7 +73,7 @@ def test_invalid_arguments_are_rejected_before_launch(lib, args, code):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 4, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 6, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -93,12 +93,14 @@ def test_config_choice_for_the_workload_shapes():
     assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (3, 256, 256, 32)
     assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (4, 8, 8, 1024, 131072)
     small = gr.selected_config(1024, 1024, 1024)
-    assert (small["config_id"], small["block_m"], small["grid"]) == (2, 128, 64)
+    assert (small["config_id"], small["block_m"], small["stages"], small["grid"]) == (5, 64, 8, 256)
+    mid = gr.selected_config(2048, 2048, 2048)
+    assert (mid["config_id"], mid["block_m"], mid["grid"]) == (4, 128, 256)
     ragged = gr.selected_config(4000, 11000, 4100)
     assert ragged["config_id"] == 1 and ragged["grid"] == 16 * 43
     assert (ragged["vec_a"], ragged["vec_b"]) == (4, 8)             # K % 8 == 4: 8-byte A loads
     skinny = gr.selected_config(64, 16384, 8192, dtype=gr.BF16)
-    assert skinny["grid"] >= 128
+    assert (skinny["config_id"], skinny["grid"]) == (5, 256)
 
 
 @pytest.mark.parametrize("K,N,a_off,b_off,want", [
@@ -115,6 +117,9 @@ def test_dma_config_falls_back_without_16_byte_loads():
     cfg = gr.selected_config(512, 512, 516, config=3)            # K % 8 != 0
     assert (cfg["config_id"], cfg["vec_a"]) == (1, 4)
     assert gr.selected_config(512, 512, 512, config=3, a_ptr=4096 + 8)["config_id"] == 1
+    for dma in (4, 5):
+        assert gr.selected_config(512, 512, 512, config=dma)["config_id"] == dma
+        assert gr.selected_config(512, 512, 516, config=dma)["config_id"] == 2
 
 
 def test_direct_config_geometry():

@@ -25,7 +25,8 @@ from tiled_dense_gemm_relu_amd import binding, inputs
 pytestmark = pytest.mark.gpu
 
 RTOL = ATOL = 1e-2
-CONFIGS = [binding.CONFIG_DIRECT, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128, binding.CONFIG_DMA_256]
+CONFIGS = [binding.CONFIG_DIRECT, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128, binding.CONFIG_DMA_256,
+           binding.CONFIG_DMA_128, binding.CONFIG_DMA_64]
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
@@ -97,8 +98,7 @@ def test_small_256_workload(config):
             assert_within_tolerance(got, want, w.dtype)
 
 
-@pytest.mark.parametrize("config", [binding.CONFIG_AUTO, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128,
-                                    binding.CONFIG_DMA_256])
+@pytest.mark.parametrize("config", [binding.CONFIG_AUTO] + CONFIGS[1:])
 def test_square_1024_workload(config):
     w = inputs.WORKLOADS["square_1024"]
     for integer in (False, True):

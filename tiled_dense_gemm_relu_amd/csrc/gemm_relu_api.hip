@@ -20,7 +20,8 @@ constexpr int kDirectTile = 32;
 
 struct Plan {
     gemm_relu_config_t cfg;
-    int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 LDS-DMA 256 kernel
+    int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 an LDS-DMA kernel (dma_id)
+    int dma_id;        // DmaId when tile == -4
     int vec_pair;      // index into kVecPairs
     int tiles_m, tiles_n;
     int c_vec_ok;
@@ -51,7 +52,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 {
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
-    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_256)
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_64)
         return GEMM_RELU_ERR_BAD_CONFIG;
     if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
 
@@ -86,24 +87,30 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     const bool full_vectors = va == 8 && vb == 8;
     int chosen = config_id;
     if (chosen == GEMM_RELU_CONFIG_AUTO) {
-        // 256x256 tiles when they yield enough workgroups to cover the 256 CUs
-        // a few times over (the LDS-DMA kernel when 16-byte loads are possible);
-        // otherwise the 128x128 tile (4x the workgroups).
+        // The largest tile that still yields enough workgroups to cover the 256
+        // CUs (192+ tiles); LDS-DMA kernels when 16-byte loads are possible.
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-        if (t256 >= 192)
-            chosen = full_vectors ? GEMM_RELU_CONFIG_DMA_256 : GEMM_RELU_CONFIG_TILE_256;
+        const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
+        if (full_vectors)
+            chosen = t256 >= 192 ? GEMM_RELU_CONFIG_DMA_256
+                   : t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_64;
         else
-            chosen = GEMM_RELU_CONFIG_TILE_128;
+            chosen = t256 >= 192 ? GEMM_RELU_CONFIG_TILE_256 : GEMM_RELU_CONFIG_TILE_128;
     }
-    if (chosen == GEMM_RELU_CONFIG_DMA_256 && !full_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
+    if (!full_vectors) {
+        if (chosen == GEMM_RELU_CONFIG_DMA_256) chosen = GEMM_RELU_CONFIG_TILE_256;
+        if (chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64) chosen = GEMM_RELU_CONFIG_TILE_128;
+    }
     plan->cfg.config_id = chosen;
 
-    if (chosen == GEMM_RELU_CONFIG_DMA_256) {
-        const TileGeom& g = kDma256Geom;
+    if (chosen >= GEMM_RELU_CONFIG_DMA_256) {
+        const int id = chosen - GEMM_RELU_CONFIG_DMA_256;
+        const TileGeom& g = kDmaGeom[id];
         if (int64_t(g.bm) * K * 2 > kMaxBand || int64_t(g.bk) * N * 2 > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
         const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
         if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
         plan->tile = -4;
+        plan->dma_id = id;
         plan->tiles_m = (int)tm;
         plan->tiles_n = (int)tn;
         plan->cfg.block_m = g.bm;
@@ -196,7 +203,8 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
     } else {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
-        const void* fn = p.tile == -4 ? ks.dma256[K % kDma256Geom.bk != 0 ? 1 : 0] : ks.tiled[p.tile][p.vec_pair];
+        const void* fn = p.tile == -4 ? ks.dma[p.dma_id][K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0]
+                                      : ks.tiled[p.tile][p.vec_pair];
         err = hipLaunchKernel(fn, dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     }
     return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;

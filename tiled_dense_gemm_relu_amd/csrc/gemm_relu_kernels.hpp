@@ -354,38 +354,36 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 
 // ---------------------------------------------------------------- LDS-DMA kernel
 
-// 256x256x32 block tile, 8 waves (4 along m x 2 along n, each 64x128), a ring
-// of 4 LDS stages filled by direct-to-LDS buffer loads
-// (buffer_load_dwordx4 ... lds): tile data goes from L2 into LDS without
-// passing through VGPRs, so loads run three K-steps ahead of the MFMAs at no
-// register cost.  This is the pages' multi-stage software pipeline
-// (T.Pipelined with several stages in flight), built from gfx950 LDS DMA
-// instead of cp.async/TMA.  Two waves share each SIMD, so one wave's LDS and
-// barrier waits are covered by the other's MFMAs.
+// Block tile BM x BN x BK, a ring of STAGES LDS stages filled by direct-to-LDS
+// buffer loads (buffer_load_dwordx4 ... lds): tile data goes from L2 into LDS
+// without passing through VGPRs, so loads run STAGES-1 K-steps ahead of the
+// MFMAs at no register cost.  This is the pages' multi-stage software
+// pipeline (T.Pipelined with several stages in flight), built from gfx950 LDS
+// DMA instead of cp.async/TMA.  The large instance (256x256x32, 4 stages)
+// runs 8 waves of 64x128, two per SIMD, so one wave's LDS and barrier waits
+// are covered by the other's MFMAs; the small instance (64x64x64, 8 stages)
+// keeps 7 stages of loads in flight for latency- and HBM-bound shapes.
 //
-// LDS layout (128 KB): A stages at [0, 64K), B stages at [64K, 128K), 16 KB
-// each, so every per-stage offset fits a ds_read immediate.
-//  * A stage, 256 rows (m) x 32 k, 64 bytes per row: chunk c (8 k values) of
-//    row r at 16 * (c ^ ((r >> 2) & 3)).  Sixteen lanes reading 16 consecutive
-//    rows at one logical chunk (one ds_read_b128) hit 16 distinct 16-byte bank
-//    groups; the swizzle is unchanged by adding a multiple of 16 rows.
-//  * B stage, 32 rows (k) x 256 n, 512 bytes per row, kept N-contiguous as it
-//    is in memory: chunk c (8 n values) of row k at 16 * (c ^ (4 * (k & 3))).
-//    MFMA operands need 8 consecutive k per lane; ds_read_b64_tr_b16 gives
-//    them: within each group of 16 lanes, source lane s points at row s / 4,
-//    columns 4 (s % 4) .. +3 of a 4 x 16 block, and lane j receives the 4 k
-//    values of column j.  The swizzle puts the 4 rows x 64 bytes that 32 lanes
-//    read at once in 16 distinct bank groups.
+// LDS layout: all A stages first, then all B stages.
+//  * A stage: BM rows (m) x BK k, K-contiguous as in memory, rows of BK*2
+//    bytes, 16-byte chunks swizzled by a_swizzle (conflict-free
+//    ds_read_b128 of 16 consecutive rows).
+//  * B stage: BK rows (k) x BN n, kept N-contiguous as it is in memory, rows
+//    of BN*2 bytes, chunks swizzled by b_swizzle.  MFMA operands need 8
+//    consecutive k per lane; ds_read_b64_tr_b16 gives them: within each group
+//    of 16 lanes, source lane s points at row s / 4, columns 4 (s % 4) .. +3 of
+//    a 4 x 16 block, and lane j receives the 4 k values of column j.
 // A DMA instruction writes 1 KB of LDS at consecutive 16-byte slots (lane l at
 // base + 16 l); the swizzle is applied by choosing which global chunk lane l
 // fetches.
 //
-// One K-step: MFMAs on the k-half already in registers, interleaved (one
-// instruction group per MFMA) with the DMA of stage kt+3 and the reads of the
-// second k-half; then wait for stage kt+1 and meet the other waves at the
-// barrier; then MFMAs on the second k-half interleaved with the reads of stage
-// kt+1's first k-half.  The loop body has no branches: stages past the end are
-// "loaded" through a zero-length buffer descriptor (nothing is fetched).
+// One K-step is BK/16 MFMA k-steps; the work of each (the next k-step's
+// fragment reads and, in the first, the DMA of stage kt+STAGES-1) is spread
+// one group per MFMA.  Before the last k-step the wave waits for stage kt+1
+// and meets the other waves at the barrier, then reads stage kt+1's first
+// fragments while the last MFMAs of stage kt run.  The loop body has no
+// branches: stages past the end are "loaded" through a zero-length buffer
+// descriptor (nothing is fetched).
 //
 // Synchronisation: the DMA loads are issued from inline assembly, so the
 // compiler does not add its own (maximal) waits before LDS reads; the kernel
@@ -432,31 +430,72 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint8_t* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
-struct DmaTile256 {
-    static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, GROUP_M = 4;
-    static constexpr int WAVES_M = 4, WAVES_N = 2, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
-    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;     // 64 x 128 per wave
+// Swizzle of the 16-byte chunks of one K-contiguous A row of ROW bytes (64 or
+// 128): chunk c of row r is stored at chunk c ^ a_swizzle(r).  Sixteen lanes
+// that read 16 consecutive rows at one logical chunk (one ds_read_b128 issue
+// group) land in 16 distinct 16-byte bank groups, and the function is
+// unchanged by adding a multiple of 16 rows.
+template <int ROW>
+__device__ __forceinline__ int a_swizzle(int r)
+{
+    static_assert(ROW == 64 || ROW == 128, "A rows of 32 or 64 k");
+    if constexpr (ROW == 64)
+        return (r >> 2) & 3;             // 4 rows share a 256-byte bank window
+    else
+        return (r ^ ((r >> 3) & 1)) & 7; // 2 rows share a 256-byte bank window
+}
+
+// Swizzle of the 16-byte chunks of one N-contiguous B row of ROW bytes (128,
+// 256 or 512).  A ds_read_b64_tr_b16 pair of 16-lane groups reads 4
+// consecutive rows (k % 4 == 0) x 4 consecutive chunks (32 columns); the XOR
+// term spreads those 16 chunks over 16 distinct bank groups.  It depends on k
+// only through bits the fragment offsets (multiples of 4 rows) leave alone.
+template <int ROW>
+__device__ __forceinline__ int b_swizzle(int k)
+{
+    static_assert(ROW == 128 || ROW == 256 || ROW == 512, "B rows of 64, 128 or 256 n");
+    if constexpr (ROW == 128)
+        return 4 * ((k >> 1) & 1);       // 2 rows share a 256-byte bank window
+    else
+        return 4 * (k & 3);              // every row starts at bank 0
+}
+
+template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
+struct DmaConfig {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, GROUP_M = GROUP_M_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;     // wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;               // 32x32 MFMA blocks per wave
-    static constexpr int STAGE_BYTES = 16384;                        // one operand, one stage
-    static constexpr int B_REGION = STAGES * STAGE_BYTES;            // B stages after the A stages
-    static constexpr int LDS_BYTES = 2 * STAGES * STAGE_BYTES;
-    static constexpr int QD = 16 / WAVES;                            // DMA instructions per wave per operand per stage
-    static constexpr int LOADS_PER_STAGE = 2 * QD;                   // per wave
-    static_assert(BM * BK * 2 == STAGE_BYTES && BK * BN * 2 == STAGE_BYTES, "stage sizes");
-    static_assert(QD * WAVES == 16, "16 DMA instructions of 1 KB fill one operand stage");
+    static constexpr int NKS = BK / 16;                              // MFMA k-steps per stage
+    static constexpr int A_ROW = BK * 2, B_ROW = BN * 2;             // bytes per LDS row
+    static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW; // bytes per stage
+    static constexpr int B_REGION = STAGES * A_STAGE;                // B stages follow the A stages
+    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+    static constexpr int QA = A_STAGE / 1024 / WAVES;                // 1 KB DMA instructions per wave per stage
+    static constexpr int QB = B_STAGE / 1024 / WAVES;
+    static constexpr int NQ = QA + QB;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of whole 32x32 MFMA blocks");
+    static_assert(BK % 32 == 0, "an even number of 16-deep MFMA k-steps per stage");
+    static_assert(QA * WAVES * 1024 == A_STAGE && QB * WAVES * 1024 == B_STAGE, "stages split into 1 KB DMAs");
+    static_assert((STAGES & (STAGES - 1)) == 0 && STAGES >= 3, "power-of-two ring of at least 3 stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+    static_assert((STAGES - 2) * NQ < 64, "vmcnt range");
 };
 
-// KTAIL: K is not a multiple of 32, so the last stage is partial and its A
+// The LDS-DMA kernel: block tile BM x BN x BK, a ring of STAGES LDS stages
+// filled by direct-to-LDS loads, WAVES_M x WAVES_N waves of 32x32 MFMA blocks.
+// KTAIL: K is not a multiple of BK, so the last stage is partial and its A
 // chunks past K are masked (K % 8 == 0 is still required).
-template <int DT, bool KTAIL>
-__global__ __launch_bounds__(DmaTile256::THREADS, 1) void gemm_relu_dma256(
+template <class Cfg, int DT, bool KTAIL>
+__global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok)
 {
-    using Cfg = DmaTile256;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES, STAGE = Cfg::STAGE_BYTES;
-    constexpr int QD = Cfg::QD, FM = Cfg::FM, FN = Cfg::FN, WTM = Cfg::WTM, WTN = Cfg::WTN;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
+    constexpr int QA = Cfg::QA, QB = Cfg::QB, NQ = Cfg::NQ, FM = Cfg::FM, FN = Cfg::FN;
+    constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN, NKS = Cfg::NKS;
+    constexpr int A_ROW = Cfg::A_ROW, B_ROW = Cfg::B_ROW;
+    constexpr int A_LANES_PER_ROW = A_ROW / 16, B_LANES_PER_ROW = B_ROW / 16;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -472,63 +511,70 @@ __global__ __launch_bounds__(DmaTile256::THREADS, 1) void gemm_relu_dma256(
     const int valid_m = min(BM, M - m0);
     const int32x4_t rsrc_a = rsrc_words(A + (size_t)m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
     const int32x4_t rsrc_none = rsrc_words(A, 0u);
-    const uint32_t lds_wave =
-        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + (uint32_t)(wave * QD * 1024);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
 
-    // DMA source offsets: wave w fills A rows [16 QD w, 16 QD (w+1)) and B
-    // rows [2 QD w, 2 QD (w+1)) of every stage.
-    uint32_t a_voff[QD], b_voff[QD];
-    int a_kcol[QD];
+    // DMA source offsets.  Every 1 KB DMA writes consecutive LDS rows; lane l
+    // fills physical chunk l % lanes-per-row of row l / lanes-per-row and so
+    // fetches the logical chunk that the swizzle puts there.
+    uint32_t a_voff[QA], b_voff[QB];
+    int a_kcol[QA];
 #pragma unroll
-    for (int q = 0; q < QD; ++q) {
-        const int row = (wave * QD + q) * 16 + (lane >> 2);
-        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+    for (int q = 0; q < QA; ++q) {
+        const int row = (wave * QA + q) * (1024 / A_ROW) + lane / A_LANES_PER_ROW;
+        const int lc = (lane % A_LANES_PER_ROW) ^ a_swizzle<A_ROW>(row);
         a_voff[q] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)lc * 16u;
         a_kcol[q] = lc * 8;
-        const int brow = (wave * QD + q) * 2 + (lane >> 5);
-        const int blc = (lane & 31) ^ (4 * (brow & 3));
-        b_voff[q] = n0 + blc * 8 < N ? (uint32_t)brow * (uint32_t)N * 2u + (uint32_t)(n0 + blc * 8) * 2u
-                                     : kOobOffset;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int row = (wave * QB + q) * (1024 / B_ROW) + lane / B_LANES_PER_ROW;
+        const int lc = (lane % B_LANES_PER_ROW) ^ b_swizzle<B_ROW>(row);
+        b_voff[q] = n0 + lc * 8 < N ? (uint32_t)row * (uint32_t)N * 2u + (uint32_t)(n0 + lc * 8) * 2u
+                                    : kOobOffset;
     }
     const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
 
-    // DMA q (0 .. QD-1: A, QD .. 2QD-1: B) of stage kt into ring slot st.
-    auto dma = [&](int kt, uint32_t st, int q) {
+    // DMA q (0 .. QA-1: A, QA .. NQ-1: B) of stage kt into ring slot `slot`.
+    // Stages past the end use a zero-length descriptor: nothing is fetched.
+    auto dma = [&](int kt, int slot, int q) {
         const int k0 = kt * BK;
         const bool live = kt < KT;
-        if (q < QD) {
+        if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
             if (KTAIL) {   // chunks past K read as zero
                 vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
                 so = 0u;
             }
-            dma_b128(live ? rsrc_a : rsrc_none, lds_wave + st + q * 1024, vo, live ? so : 0u);
+            dma_b128(live ? rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 1024, vo,
+                     live ? so : 0u);
         } else {
             const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
             const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N, nb) : rsrc_none;
-            dma_b128(rb, lds_wave + Cfg::B_REGION + st + (q - QD) * 1024, b_voff[q - QD], 0u);
+            dma_b128(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + (q - QA)) * 1024,
+                     b_voff[q - QA], 0u);
         }
     };
 
     // Per-lane LDS read offsets inside a stage.
-    //  A fragment j, k-half ks: row wm*WTM + 32j + lane%32, chunk 2ks + lane/32.
-    uint32_t a_frag_off[2];
+    //  A fragment j, k-step ks: row wm*WTM + 32j + lane%32, chunk 2ks + lane/32.
+    uint32_t a_frag_off[NKS];
     {
         const int row = wm * WTM + (lane & 31);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            a_frag_off[ks] = (uint32_t)(row * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)));
+        for (int ks = 0; ks < NKS; ++ks)
+            a_frag_off[ks] = (uint32_t)(row * A_ROW + 16 * ((2 * ks + (lane >> 5)) ^ a_swizzle<A_ROW>(row)));
     }
-    //  B^T fragment i, k-half ks, half hh: lane group g = lane/16, j = lane%16;
+    //  B^T fragment i, k-step ks, half hh: lane group g = lane/16, j = lane%16;
     //  row k = 16ks + 8(g/2) + 4hh + j/4, column n = wn*WTN + 32i + 16(g%2) + 4(j%4).
     uint32_t b_frag_off[FN];
     {
         const int g = lane >> 4, j = lane & 15;
-        const int krow = 8 * (g >> 1) + (j >> 2);          // + 16ks + 4hh, which keep k & 3
+        const int krow = 8 * (g >> 1) + (j >> 2);          // + 16ks + 4hh leave the swizzle unchanged
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
             const int n = wn * WTN + i * 32 + 16 * (g & 1) + 4 * (j & 3);
-            b_frag_off[i] = (uint32_t)(Cfg::B_REGION + krow * 512 + 16 * ((n >> 3) ^ (4 * (krow & 3))) + 8 * (j & 1));
+            b_frag_off[i] = (uint32_t)(Cfg::B_REGION + krow * B_ROW +
+                                       16 * ((n >> 3) ^ b_swizzle<B_ROW>(krow)) + 8 * (j & 1));
         }
     }
 
@@ -538,55 +584,63 @@ __global__ __launch_bounds__(DmaTile256::THREADS, 1) void gemm_relu_dma256(
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = floatx16{0};
 
-    // [k-half][fragment]: B^T fragments (MFMA A operand) and A fragments (MFMA B operand)
+    // [buffer][fragment]: B^T fragments (MFMA A operand) and A fragments (MFMA B operand)
     u32x4 fa[2][FN], fb[2][FM];
-    auto read_a = [&](int buf, uint32_t st, int ks, int j) {
-        fb[buf][j] = *reinterpret_cast<const u32x4*>(smem + st + a_frag_off[ks] + j * 32 * 64);
+    auto read_a = [&](int buf, int slot, int ks, int j) {
+        fb[buf][j] = *reinterpret_cast<const u32x4*>(smem + slot * Cfg::A_STAGE + a_frag_off[ks] + j * 32 * A_ROW);
     };
-    auto read_b = [&](int buf, uint32_t st, int ks, int i) {
-        const u32x2 lo = ds_read_tr16(smem + st + b_frag_off[i] + (16 * ks + 0) * 512);
-        const u32x2 hi = ds_read_tr16(smem + st + b_frag_off[i] + (16 * ks + 4) * 512);
+    auto read_b = [&](int buf, int slot, int ks, int i) {
+        const uint8_t* p = smem + slot * Cfg::B_STAGE + b_frag_off[i] + 16 * ks * B_ROW;
+        const u32x2 lo = ds_read_tr16(p);
+        const u32x2 hi = ds_read_tr16(p + 4 * B_ROW);
         fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
     };
-    auto mfma1 = [&](int buf, int t) {
-        const int i = t / FM, j = t % FM;
-        acc[i][j] = mfma_32x32x16<DT>(fa[buf][i], fb[buf][j], acc[i][j]);
+    auto read_unit = [&](int buf, int slot, int ks, int u) {
+        if (u < FM) read_a(buf, slot, ks, u);
+        else read_b(buf, slot, ks, u - FM);
     };
-    constexpr int NQ = Cfg::LOADS_PER_STAGE, NF = FM + FN, NMF = FM * FN;
-    static_assert(NQ <= NMF && NF <= NMF, "one DMA and one fragment read per MFMA slot");
+    constexpr int NF = FM + FN, NMF = FM * FN;
 
-    // Prologue: stages 0..2 in flight, stage 0 landed, its first k-half read.
+    // Prologue: stages 0 .. S-2 in flight, stage 0 landed, its first k-step read.
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) dma(s, s * STAGE, q);
+        for (int q = 0; q < NQ; ++q) dma(s, s, q);
     wait_vmcnt<(S - 2) * NQ>();
     lds_barrier();
 #pragma unroll
-    for (int j = 0; j < FM; ++j) read_a(0, 0, 0, j);
-#pragma unroll
-    for (int i = 0; i < FN; ++i) read_b(0, 0, 0, i);
+    for (int u = 0; u < NF; ++u) read_unit(0, 0, 0, u);
 
     for (int kt = 0; kt < KT; ++kt) {
-        const uint32_t st = (uint32_t)(kt & (S - 1)) * STAGE;
-        const uint32_t stn = (uint32_t)((kt + 1) & (S - 1)) * STAGE;
-        const uint32_t sti = (uint32_t)((kt + S - 1) & (S - 1)) * STAGE;   // slot of stage kt-1, free since the last barrier
+        const int slot = kt & (S - 1);
+        const int slot_next = (kt + 1) & (S - 1);
+        const int slot_fill = (kt + S - 1) & (S - 1);   // stage kt-1's slot: free since the last barrier
 #pragma unroll
-        for (int t = 0; t < NMF; ++t) {
-            mfma1(0, t);
-            if (t < NQ) dma(kt + S - 1, sti, t);
-            if (t < FM) read_a(1, st, 1, t);
-            else if (t < NF) read_b(1, st, 1, t - FM);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        wait_vmcnt<(S - 2) * NQ>();        // stage kt+1 landed (for this wave)
-        lds_barrier();                     // ... and for every wave
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int cur = ks & 1, nxt = cur ^ 1;
+            const bool last = ks == NKS - 1;
+            if (last) {
+                wait_vmcnt<(S - 2) * NQ>();   // stage kt+1 landed (for this wave)
+                lds_barrier();                // ... and for every wave
+            }
+            // Work spread over this k-step's MFMAs: the next k-step's fragment
+            // reads (from the next stage after the barrier), then, in the first
+            // k-step, the DMAs of stage kt+S-1.
+            const int n_items = NF + (ks == 0 ? NQ : 0);
 #pragma unroll
-        for (int t = 0; t < NMF; ++t) {
-            mfma1(1, t);
-            if (t < FM) read_a(0, stn, 0, t);
-            else if (t < NF) read_b(0, stn, 0, t - FM);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < NMF; ++t) {
+                acc[t / FM][t % FM] = mfma_32x32x16<DT>(fa[cur][t / FM], fb[cur][t % FM], acc[t / FM][t % FM]);
+#pragma unroll
+                for (int u = t * n_items / NMF; u < (t + 1) * n_items / NMF; ++u) {
+                    if (u < NF) {
+                        if (last) read_unit(nxt, slot_next, 0, u);
+                        else read_unit(nxt, slot, ks + 1, u);
+                    } else {
+                        dma(kt + S - 1, slot_fill, u - NF);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
@@ -599,6 +653,11 @@ __global__ __launch_bounds__(DmaTile256::THREADS, 1) void gemm_relu_dma256(
             store_block<DT>(C, acc[i][j], lane, m0 + wm * WTM + j * 32, n0 + wn * WTN + i * 32, M, N,
                             c_vec_ok != 0);
 }
+
+// Instances.
+using DmaTile256 = DmaConfig<256, 256, 32, 4, 4, 2, 4>;   // large shapes: 8 waves of 64x128
+using DmaTile128 = DmaConfig<128, 128, 64, 4, 2, 2, 4>;   // mid shapes: 4 waves of 64x64
+using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny shapes: 4 waves of 32x32, 8 stages
 
 // ---------------------------------------------------------------- direct kernel
 

@@ -24,11 +24,17 @@ constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 
 struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
     const void* direct;
-    const void* dma256[2];   // 256x256x32, 4 LDS-DMA stages; [K % 32 != 0]; needs 8-element loads of A and B
+    const void* dma[3][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
 };
 
-// Geometry of the LDS-DMA kernel (must match DmaTile256).
-constexpr TileGeom kDma256Geom = {256, 256, 32, 4, 512, 4};
+// LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.
+enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kNumDma = 3 };
+// Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64).
+constexpr TileGeom kDmaGeom[kNumDma] = {
+    {256, 256, 32, 4, 512, 4},
+    {128, 128, 64, 4, 256, 4},
+    {64, 64, 64, 8, 256, 4},
+};
 
 const DtypeKernels& kernels_f16();
 const DtypeKernels& kernels_bf16();

@@ -14,9 +14,12 @@ constexpr bool geom_matches = Cfg::BM == kTileGeom[id].bm && Cfg::BN == kTileGeo
                               Cfg::THREADS == kTileGeom[id].threads && Cfg::GROUP_M == kTileGeom[id].group_m;
 static_assert(geom_matches<Tile256, kTile256> && geom_matches<Tile128, kTile128>,
               "host tile table out of date");
-static_assert(DmaTile256::BM == kDma256Geom.bm && DmaTile256::BN == kDma256Geom.bn &&
-                  DmaTile256::BK == kDma256Geom.bk && DmaTile256::STAGES == kDma256Geom.stages &&
-                  DmaTile256::THREADS == kDma256Geom.threads && DmaTile256::GROUP_M == kDma256Geom.group_m,
+template <class Cfg, int id>
+constexpr bool dma_geom_matches = Cfg::BM == kDmaGeom[id].bm && Cfg::BN == kDmaGeom[id].bn &&
+                                  Cfg::BK == kDmaGeom[id].bk && Cfg::STAGES == kDmaGeom[id].stages &&
+                                  Cfg::THREADS == kDmaGeom[id].threads && Cfg::GROUP_M == kDmaGeom[id].group_m;
+static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
+                  dma_geom_matches<DmaTile64, kDma64>,
               "host DMA tile geometry out of date");
 
 template <class Cfg>
@@ -36,8 +39,12 @@ DtypeKernels make_table()
     fill_row<Tile256>(t.tiled[kTile256]);
     fill_row<Tile128>(t.tiled[kTile128]);
     t.direct = (const void*)&gemm_relu_direct<kBF16>;
-    t.dma256[0] = (const void*)&gemm_relu_dma256<kBF16, false>;
-    t.dma256[1] = (const void*)&gemm_relu_dma256<kBF16, true>;
+    t.dma[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256, kBF16, false>;
+    t.dma[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256, kBF16, true>;
+    t.dma[kDma128][0] = (const void*)&gemm_relu_dma<DmaTile128, kBF16, false>;
+    t.dma[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128, kBF16, true>;
+    t.dma[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64, kBF16, false>;
+    t.dma[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64, kBF16, true>;
     return t;
 }
 }  // namespace
