@@ -72,9 +72,10 @@ enum {
     GEMM_RELU_CONFIG_DMA_128 = 4,     /* 128x128x64 block tile, 4 waves, 4 direct-to-LDS stages */
     GEMM_RELU_CONFIG_DMA_64 = 5       /* 64x64x64 block tile, 4 waves, 8 direct-to-LDS stages
                                          (small, skinny and bandwidth-bound shapes) */
-    /* The DMA_* kernels need 16-byte loads of A and B (K % 8 == 0, N % 8 == 0, 16-byte
-       aligned A and B); for other inputs a DMA_* request falls back to TILE_256 (DMA_256)
-       or TILE_128 (DMA_128, DMA_64). */
+    /* DMA_128 and DMA_64 need 16-byte loads of A and B (K % 8 == 0, N % 8 == 0, 16-byte
+       aligned A and B); DMA_256 also takes 4-byte loads (K and N even, 4-byte aligned A and B).
+       For other inputs a DMA_* request falls back to TILE_256 (DMA_256) or TILE_128
+       (DMA_128, DMA_64). */
 };
 
 /* What a configuration is, for reports and tests. */

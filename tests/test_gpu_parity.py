@@ -70,7 +70,9 @@ INT_SHAPES = [(1, 1, 1), (32, 32, 16), (33, 65, 17), (255, 257, 63), (257, 255, 
               (300, 520, 130), (129, 131, 200), (512, 256, 192), (64, 1000, 1024),
               # 16-byte-loadable shapes for the LDS-DMA kernel: a K tail (K % 32 != 0),
               # fewer K-steps than pipeline stages, and M / N tails
-              (300, 520, 200), (256, 256, 40), (64, 64, 8), (257, 264, 96), (520, 776, 1064)]
+              (300, 520, 200), (256, 256, 40), (64, 64, 8), (257, 264, 96), (520, 776, 1064),
+              # 4-byte DMA lanes: A rows of an even length, B rows of an even length, both
+              (200, 264, 100), (260, 262, 64), (256, 300, 66), (300, 270, 4098)]
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])

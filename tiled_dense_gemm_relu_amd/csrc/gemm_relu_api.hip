@@ -22,6 +22,7 @@ struct Plan {
     gemm_relu_config_t cfg;
     int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 an LDS-DMA kernel (dma_id)
     int dma_id;        // DmaId when tile == -4
+    int dma_a4, dma_b4;    // 4-byte DMA lanes for A / B (256 LDS-DMA kernel only)
     int vec_pair;      // index into kVecPairs
     int tiles_m, tiles_n;
     int c_vec_ok;
@@ -85,22 +86,25 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 
     const int va = vec_width(A, K), vb = vec_width(B, N);
     const bool full_vectors = va == 8 && vb == 8;
+    // 4-byte DMA lanes work for rows of an even length with 4-byte aligned bases.
+    const bool dword_vectors = va >= 2 && vb >= 2;
     int chosen = config_id;
     if (chosen == GEMM_RELU_CONFIG_AUTO) {
         // The largest tile that still yields enough workgroups to cover the 256
-        // CUs (192+ tiles); LDS-DMA kernels when 16-byte loads are possible.
+        // CUs (192+ tiles); LDS-DMA kernels when 16-byte loads are possible (the
+        // 256 tile also with 4-byte loads).
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
-        if (full_vectors)
-            chosen = t256 >= 192 ? GEMM_RELU_CONFIG_DMA_256
-                   : t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_64;
+        if (t256 >= 192)
+            chosen = dword_vectors ? GEMM_RELU_CONFIG_DMA_256 : GEMM_RELU_CONFIG_TILE_256;
+        else if (full_vectors)
+            chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_64;
         else
-            chosen = t256 >= 192 ? GEMM_RELU_CONFIG_TILE_256 : GEMM_RELU_CONFIG_TILE_128;
+            chosen = GEMM_RELU_CONFIG_TILE_128;
     }
-    if (!full_vectors) {
-        if (chosen == GEMM_RELU_CONFIG_DMA_256) chosen = GEMM_RELU_CONFIG_TILE_256;
-        if (chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64) chosen = GEMM_RELU_CONFIG_TILE_128;
-    }
+    if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
+    if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64) && !full_vectors)
+        chosen = GEMM_RELU_CONFIG_TILE_128;
     plan->cfg.config_id = chosen;
 
     if (chosen >= GEMM_RELU_CONFIG_DMA_256) {
@@ -118,8 +122,10 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         plan->cfg.block_k = g.bk;
         plan->cfg.stages = g.stages;
         plan->cfg.threads = g.threads;
-        plan->cfg.vec_a = 8;
-        plan->cfg.vec_b = 8;
+        plan->dma_a4 = va < 8 ? 1 : 0;     // only the 256 kernel gets here with va or vb < 8
+        plan->dma_b4 = vb < 8 ? 1 : 0;
+        plan->cfg.vec_a = va < 8 ? 2 : 8;
+        plan->cfg.vec_b = vb < 8 ? 2 : 8;
         plan->cfg.grid = tm * tn;
         plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2;
         return GEMM_RELU_OK;
@@ -203,8 +209,10 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
     } else {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
-        const void* fn = p.tile == -4 ? ks.dma[p.dma_id][K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0]
-                                      : ks.tiled[p.tile][p.vec_pair];
+        const int ktail = p.tile == -4 && K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0;
+        const void* fn = p.tile != -4 ? ks.tiled[p.tile][p.vec_pair]
+                       : p.dma_id == kDma256 ? ks.dma256_dw[p.dma_a4][p.dma_b4][ktail]
+                                             : ks.dma[p.dma_id][ktail];
         err = hipLaunchKernel(fn, dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     }
     return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;

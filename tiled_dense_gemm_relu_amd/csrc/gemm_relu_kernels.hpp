@@ -410,6 +410,15 @@ __device__ __forceinline__ void dma_b128(int32x4_t rsrc, uint32_t lds_addr, uint
                  : "memory", "m0");
 }
 
+// 64 lanes x 4 bytes from the buffer into LDS [lds_addr, lds_addr + 256).
+__device__ __forceinline__ void dma_b32(int32x4_t rsrc, uint32_t lds_addr, uint32_t voffset, uint32_t soffset)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+                 : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -460,7 +469,8 @@ __device__ __forceinline__ int b_swizzle(int k)
         return 4 * (k & 3);              // every row starts at bank 0
 }
 
-template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
+template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_,
+          int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16>
 struct DmaConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, GROUP_M = GROUP_M_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
@@ -471,12 +481,19 @@ struct DmaConfig {
     static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW; // bytes per stage
     static constexpr int B_REGION = STAGES * A_STAGE;                // B stages follow the A stages
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
-    static constexpr int QA = A_STAGE / 1024 / WAVES;                // 1 KB DMA instructions per wave per stage
-    static constexpr int QB = B_STAGE / 1024 / WAVES;
+    // Bytes each lane moves per DMA instruction: 16 (buffer_load_dwordx4, needs
+    // rows of a multiple of 8 elements) or 4 (buffer_load_dword, rows of an even
+    // number of elements).
+    static constexpr int A_LANE_BYTES = A_LANE_BYTES_, B_LANE_BYTES = B_LANE_BYTES_;
+    static constexpr int QA = A_STAGE / (64 * A_LANE_BYTES) / WAVES; // DMA instructions per wave per stage
+    static constexpr int QB = B_STAGE / (64 * B_LANE_BYTES) / WAVES;
     static constexpr int NQ = QA + QB;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of whole 32x32 MFMA blocks");
     static_assert(BK % 32 == 0, "an even number of 16-deep MFMA k-steps per stage");
-    static_assert(QA * WAVES * 1024 == A_STAGE && QB * WAVES * 1024 == B_STAGE, "stages split into 1 KB DMAs");
+    static_assert((A_LANE_BYTES == 16 || A_LANE_BYTES == 4) && (B_LANE_BYTES == 16 || B_LANE_BYTES == 4),
+                  "dwordx4 or dword DMA");
+    static_assert(QA * WAVES * 64 * A_LANE_BYTES == A_STAGE && QB * WAVES * 64 * B_LANE_BYTES == B_STAGE,
+                  "stages split evenly into DMA instructions");
     static_assert((STAGES & (STAGES - 1)) == 0 && STAGES >= 3, "power-of-two ring of at least 3 stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
     static_assert((STAGES - 2) * NQ < 64, "vmcnt range");
@@ -485,7 +502,8 @@ struct DmaConfig {
 // The LDS-DMA kernel: block tile BM x BN x BK, a ring of STAGES LDS stages
 // filled by direct-to-LDS loads, WAVES_M x WAVES_N waves of 32x32 MFMA blocks.
 // KTAIL: K is not a multiple of BK, so the last stage is partial and its A
-// chunks past K are masked (K % 8 == 0 is still required).
+// pieces past K are masked (K must still be a multiple of the piece: 8
+// elements for 16-byte lanes, 2 for 4-byte lanes).
 template <class Cfg, int DT, bool KTAIL>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
@@ -495,7 +513,6 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     constexpr int QA = Cfg::QA, QB = Cfg::QB, NQ = Cfg::NQ, FM = Cfg::FM, FN = Cfg::FN;
     constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN, NKS = Cfg::NKS;
     constexpr int A_ROW = Cfg::A_ROW, B_ROW = Cfg::B_ROW;
-    constexpr int A_LANES_PER_ROW = A_ROW / 16, B_LANES_PER_ROW = B_ROW / 16;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -513,27 +530,36 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const int32x4_t rsrc_none = rsrc_words(A, 0u);
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
 
-    // DMA source offsets.  Every 1 KB DMA writes consecutive LDS rows; lane l
-    // fills physical chunk l % lanes-per-row of row l / lanes-per-row and so
-    // fetches the logical chunk that the swizzle puts there.
+    // DMA source offsets.  A DMA instruction writes 64 * LANE_BYTES consecutive
+    // LDS bytes, lane l at byte l * LANE_BYTES; that byte lies in some row and
+    // physical 16-byte chunk of the stage, and the lane fetches the logical
+    // chunk (and the same bytes inside it) that the swizzle puts there.
+    constexpr int LA = Cfg::A_LANE_BYTES, LB = Cfg::B_LANE_BYTES;
     uint32_t a_voff[QA], b_voff[QB];
     int a_kcol[QA];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-        const int row = (wave * QA + q) * (1024 / A_ROW) + lane / A_LANES_PER_ROW;
-        const int lc = (lane % A_LANES_PER_ROW) ^ a_swizzle<A_ROW>(row);
-        a_voff[q] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)lc * 16u;
-        a_kcol[q] = lc * 8;
+        const int byte = ((wave * QA + q) * 64 + lane) * LA;       // offset inside the A stage
+        const int row = byte / A_ROW;
+        const int lc = ((byte % A_ROW) / 16) ^ a_swizzle<A_ROW>(row);
+        const int kcol = lc * 8 + (byte % 16) / 2;                  // first k of this lane's piece
+        a_voff[q] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)kcol * 2u;
+        a_kcol[q] = kcol;
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-        const int row = (wave * QB + q) * (1024 / B_ROW) + lane / B_LANES_PER_ROW;
-        const int lc = (lane % B_LANES_PER_ROW) ^ b_swizzle<B_ROW>(row);
-        b_voff[q] = n0 + lc * 8 < N ? (uint32_t)row * (uint32_t)N * 2u + (uint32_t)(n0 + lc * 8) * 2u
-                                    : kOobOffset;
+        const int byte = ((wave * QB + q) * 64 + lane) * LB;       // offset inside the B stage
+        const int row = byte / B_ROW;
+        const int lc = ((byte % B_ROW) / 16) ^ b_swizzle<B_ROW>(row);
+        const int col = n0 + lc * 8 + (byte % 16) / 2;               // first n of this lane's piece
+        b_voff[q] = col < N ? (uint32_t)row * (uint32_t)N * 2u + (uint32_t)col * 2u : kOobOffset;
     }
     const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
 
+    auto dma_issue = [&](int32x4_t rsrc, uint32_t lds, uint32_t vo, uint32_t so, int lane_bytes) {
+        if (lane_bytes == 16) dma_b128(rsrc, lds, vo, so);
+        else dma_b32(rsrc, lds, vo, so);
+    };
     // DMA q (0 .. QA-1: A, QA .. NQ-1: B) of stage kt into ring slot `slot`.
     // Stages past the end use a zero-length descriptor: nothing is fetched.
     auto dma = [&](int kt, int slot, int q) {
@@ -541,17 +567,17 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         const bool live = kt < KT;
         if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
-            if (KTAIL) {   // chunks past K read as zero
+            if (KTAIL) {   // pieces past K read as zero (K is a multiple of the piece length)
                 vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
                 so = 0u;
             }
-            dma_b128(live ? rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 1024, vo,
-                     live ? so : 0u);
+            dma_issue(live ? rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 64 * LA, vo,
+                      live ? so : 0u, LA);
         } else {
             const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
             const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N, nb) : rsrc_none;
-            dma_b128(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + (q - QA)) * 1024,
-                     b_voff[q - QA], 0u);
+            dma_issue(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + (q - QA)) * 64 * LB,
+                      b_voff[q - QA], 0u, LB);
         }
     };
 
@@ -656,6 +682,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
 
 // Instances.
 using DmaTile256 = DmaConfig<256, 256, 32, 4, 4, 2, 4>;   // large shapes: 8 waves of 64x128
+using DmaTile256A4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 16>;   // ... with A rows of an even length
+using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;   // ... with B rows of an even length
+using DmaTile256AB4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4>;   // ... both
 using DmaTile128 = DmaConfig<128, 128, 64, 4, 2, 2, 4>;   // mid shapes: 4 waves of 64x64
 using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny shapes: 4 waves of 32x32, 8 stages
 

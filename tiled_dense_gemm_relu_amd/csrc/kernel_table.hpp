@@ -25,6 +25,9 @@ struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
     const void* direct;
     const void* dma[3][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
+    // The 256 LDS-DMA kernel with 4-byte DMA lanes: [A 4-byte][B 4-byte][K % BK != 0]
+    // (index [0][0] unused: that is dma[kDma256]); need 2-element loads.
+    const void* dma256_dw[2][2][2];
 };
 
 // LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.

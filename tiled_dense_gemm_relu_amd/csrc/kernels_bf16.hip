@@ -45,6 +45,14 @@ DtypeKernels make_table()
     t.dma[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128, kBF16, true>;
     t.dma[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64, kBF16, false>;
     t.dma[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64, kBF16, true>;
+    t.dma256_dw[0][0][0] = t.dma[kDma256][0];
+    t.dma256_dw[0][0][1] = t.dma[kDma256][1];
+    t.dma256_dw[1][0][0] = (const void*)&gemm_relu_dma<DmaTile256A4, kBF16, false>;
+    t.dma256_dw[1][0][1] = (const void*)&gemm_relu_dma<DmaTile256A4, kBF16, true>;
+    t.dma256_dw[0][1][0] = (const void*)&gemm_relu_dma<DmaTile256B4, kBF16, false>;
+    t.dma256_dw[0][1][1] = (const void*)&gemm_relu_dma<DmaTile256B4, kBF16, true>;
+    t.dma256_dw[1][1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, kBF16, false>;
+    t.dma256_dw[1][1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, kBF16, true>;
     return t;
 }
 }  // namespace
