@@ -88,7 +88,8 @@ typedef struct {
     int threads;      /* threads per workgroup */
     int vec_a;        /* elements per global load of A (1, 2, 4 or 8) */
     int vec_b;        /* elements per global load of B */
-    int64_t grid;     /* workgroups launched */
+    int64_t grid;     /* output tiles; workgroups launched, except for the DMA_* kernels, which
+                         run one persistent workgroup per CU (at most one per tile) */
     int lds_bytes;    /* LDS per workgroup */
 } gemm_relu_config_t;
 

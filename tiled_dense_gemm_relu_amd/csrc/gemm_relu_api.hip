@@ -174,26 +174,32 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     return GEMM_RELU_OK;
 }
 
-// Per-device cache: 0 unknown, 1 gfx950, -1 something else.
-std::atomic<int> g_device_ok[64];
+// Per-device cache: 0 unknown, > 0 gfx950 with that many CUs, -1 something else.
+std::atomic<int> g_device_cus[64];
 
-int check_device()
+// Checks that the current device is a gfx950 and returns its CU count in *cus.
+int check_device(int* cus)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_RELU_ERR_NO_DEVICE;
     if (dev < 64) {
-        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
-        if (known != 0) return known > 0 ? GEMM_RELU_OK : GEMM_RELU_ERR_NO_DEVICE;
+        const int known = g_device_cus[dev].load(std::memory_order_relaxed);
+        if (known != 0) {
+            *cus = known;
+            return known > 0 ? GEMM_RELU_OK : GEMM_RELU_ERR_NO_DEVICE;
+        }
     }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_RELU_ERR_NO_DEVICE;
-    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < 64) g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.multiProcessorCount > 0;
+    const int value = ok ? prop.multiProcessorCount : -1;
+    if (dev < 64) g_device_cus[dev].store(value, std::memory_order_relaxed);
+    *cus = value;
     return ok ? GEMM_RELU_OK : GEMM_RELU_ERR_NO_DEVICE;
 }
 
 int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
-           hipStream_t stream)
+           int cus, hipStream_t stream)
 {
     const DtypeKernels& ks = dtype == GEMM_RELU_F16 ? kernels_f16() : kernels_bf16();
     int m = (int)M, n = (int)N, k = (int)K;
@@ -213,7 +219,10 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
         const void* fn = p.tile != -4 ? ks.tiled[p.tile][p.vec_pair]
                        : p.dma_id == kDma256 ? ks.dma256_dw[p.dma_a4][p.dma_b4][ktail]
                                              : ks.dma[p.dma_id][ktail];
-        err = hipLaunchKernel(fn, dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
+        // The LDS-DMA kernels are persistent: one workgroup per CU (their LDS
+        // ring fills a CU), each walking every grid-th tile.
+        const int64_t grid = p.tile == -4 ? std::min<int64_t>(p.cfg.grid, cus) : p.cfg.grid;
+        err = hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     }
     return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;
 }
@@ -241,9 +250,10 @@ int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int6
     int rc = make_plan(A, B, C, M, N, K, dtype, config_id, &p);
     if (rc != GEMM_RELU_OK) return rc;
     if (p.tile == -3) return GEMM_RELU_OK;          // M == 0 or N == 0
-    rc = check_device();
+    int cus = 0;
+    rc = check_device(&cus);
     if (rc != GEMM_RELU_OK) return rc;
-    return launch(p, A, B, C, M, N, K, dtype, static_cast<hipStream_t>(stream));
+    return launch(p, A, B, C, M, N, K, dtype, cus, static_cast<hipStream_t>(stream));
 }
 
 int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype, void* stream)

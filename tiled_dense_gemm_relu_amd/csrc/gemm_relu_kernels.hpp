@@ -389,6 +389,11 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 // compiler does not add its own (maximal) waits before LDS reads; the kernel
 // waits for exactly the loads of the stage it is about to read
 // (s_waitcnt vmcnt) before the barrier.
+//
+// The workgroups are persistent (one per CU): each computes every G-th tile
+// and streams the K-steps of all its tiles through one ring, so a tile's
+// first stages are already in LDS when the previous tile's epilogue runs, and
+// no workgroup is dispatched, started or drained between tiles.
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
@@ -494,7 +499,7 @@ struct DmaConfig {
                   "dwordx4 or dword DMA");
     static_assert(QA * WAVES * 64 * A_LANE_BYTES == A_STAGE && QB * WAVES * 64 * B_LANE_BYTES == B_STAGE,
                   "stages split evenly into DMA instructions");
-    static_assert((STAGES & (STAGES - 1)) == 0 && STAGES >= 3, "power-of-two ring of at least 3 stages");
+    static_assert((STAGES & (STAGES - 1)) == 0 && STAGES >= 2, "power-of-two ring of at least 2 stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
     static_assert((STAGES - 2) * NQ < 64, "vmcnt range");
 };
@@ -519,24 +524,32 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    // Persistent workgroups: workgroup b computes tiles b, b + G, b + 2G, ...
+    // (G = gridDim.x, a multiple of 8 or all tiles), and all K-steps of all its
+    // tiles form one stream through the LDS ring, so the first stages of the
+    // next tile are loaded while the current tile finishes.
+    const int total_tiles = tiles_m * tiles_n;
+    const int n_tiles = (total_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int KT = (K + BK - 1) / BK;
+    const int steps = n_tiles * KT;
+    auto tile_origin = [&](int i, int& m0, int& n0) {
+        int tm, tn;
+        tile_coords((int)blockIdx.x + i * (int)gridDim.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    };
 
-    // A: rows m0 .. m0 + valid_m - 1 of A; rows past M read as zero.
-    const int valid_m = min(BM, M - m0);
-    const int32x4_t rsrc_a = rsrc_words(A + (size_t)m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
     const int32x4_t rsrc_none = rsrc_words(A, 0u);
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
 
-    // DMA source offsets.  A DMA instruction writes 64 * LANE_BYTES consecutive
-    // LDS bytes, lane l at byte l * LANE_BYTES; that byte lies in some row and
-    // physical 16-byte chunk of the stage, and the lane fetches the logical
-    // chunk (and the same bytes inside it) that the swizzle puts there.
+    // DMA source offsets, relative to the tile origin.  A DMA instruction writes
+    // 64 * LANE_BYTES consecutive LDS bytes, lane l at byte l * LANE_BYTES; that
+    // byte lies in some row and physical 16-byte chunk of the stage, and the
+    // lane fetches the logical chunk (and the same bytes inside it) that the
+    // swizzle puts there.
     constexpr int LA = Cfg::A_LANE_BYTES, LB = Cfg::B_LANE_BYTES;
     uint32_t a_voff[QA], b_voff[QB];
-    int a_kcol[QA];
+    int a_kcol[QA], b_ncol[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
         const int byte = ((wave * QA + q) * 64 + lane) * LA;       // offset inside the A stage
@@ -551,33 +564,57 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         const int byte = ((wave * QB + q) * 64 + lane) * LB;       // offset inside the B stage
         const int row = byte / B_ROW;
         const int lc = ((byte % B_ROW) / 16) ^ b_swizzle<B_ROW>(row);
-        const int col = n0 + lc * 8 + (byte % 16) / 2;               // first n of this lane's piece
-        b_voff[q] = col < N ? (uint32_t)row * (uint32_t)N * 2u + (uint32_t)col * 2u : kOobOffset;
+        const int ncol = lc * 8 + (byte % 16) / 2;                  // first n of this lane's piece, from n0
+        b_voff[q] = (uint32_t)row * (uint32_t)N * 2u + (uint32_t)ncol * 2u;
+        b_ncol[q] = ncol;
     }
     const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
+
+    // The load side of the stream: the tile and K-step the next DMA belongs to.
+    int f_tile = 0, f_kt = 0, f_m0 = 0, f_n0 = 0;
+    int32x4_t f_rsrc_a = rsrc_none;
+    auto fill_tile_setup = [&]() {
+        if (f_tile < n_tiles) {
+            tile_origin(f_tile, f_m0, f_n0);
+            // rows f_m0 .. f_m0 + valid_m - 1 of A; rows past M read as zero
+            const int valid_m = min(BM, M - f_m0);
+            f_rsrc_a = rsrc_words(A + (size_t)f_m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
+        }
+    };
+    fill_tile_setup();
 
     auto dma_issue = [&](int32x4_t rsrc, uint32_t lds, uint32_t vo, uint32_t so, int lane_bytes) {
         if (lane_bytes == 16) dma_b128(rsrc, lds, vo, so);
         else dma_b32(rsrc, lds, vo, so);
     };
-    // DMA q (0 .. QA-1: A, QA .. NQ-1: B) of stage kt into ring slot `slot`.
-    // Stages past the end use a zero-length descriptor: nothing is fetched.
-    auto dma = [&](int kt, int slot, int q) {
-        const int k0 = kt * BK;
-        const bool live = kt < KT;
+    // DMA q (0 .. QA-1: A, QA .. NQ-1: B) of the current fill step into ring
+    // slot `slot`.  Steps past the end of the stream use a zero-length
+    // descriptor: nothing is fetched.
+    auto dma = [&](int slot, int q) {
+        const int k0 = f_kt * BK;
+        const bool live = f_tile < n_tiles;
         if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
             if (KTAIL) {   // pieces past K read as zero (K is a multiple of the piece length)
                 vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
                 so = 0u;
             }
-            dma_issue(live ? rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 64 * LA, vo,
+            dma_issue(live ? f_rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 64 * LA, vo,
                       live ? so : 0u, LA);
         } else {
+            // descriptor based at (row k0, column f_n0): rows past K read as zero
             const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
-            const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N, nb) : rsrc_none;
-            dma_issue(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + (q - QA)) * 64 * LB,
-                      b_voff[q - QA], 0u, LB);
+            const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N + f_n0, nb) : rsrc_none;
+            const uint32_t vo = f_n0 + b_ncol[q - QA] < N ? b_voff[q - QA] : kOobOffset;   // columns past N
+            dma_issue(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + (q - QA)) * 64 * LB, vo, 0u,
+                      LB);
+        }
+    };
+    auto fill_advance = [&]() {
+        if (++f_kt == KT) {
+            f_kt = 0;
+            ++f_tile;
+            fill_tile_setup();
         }
     };
 
@@ -627,31 +664,37 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     };
     constexpr int NF = FM + FN, NMF = FM * FN;
 
-    // Prologue: stages 0 .. S-2 in flight, stage 0 landed, its first k-step read.
+    // The compute side of the stream: the tile being accumulated.
+    int c_tile = 0, c_kt = 0, c_m0, c_n0;
+    tile_origin(0, c_m0, c_n0);
+
+    // Prologue: steps 0 .. S-2 in flight, step 0 landed, its first k-step read.
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
+    for (int s = 0; s < S - 1; ++s) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) dma(s, s, q);
+        for (int q = 0; q < NQ; ++q) dma(s, q);
+        fill_advance();
+    }
     wait_vmcnt<(S - 2) * NQ>();
     lds_barrier();
 #pragma unroll
     for (int u = 0; u < NF; ++u) read_unit(0, 0, 0, u);
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const int slot = kt & (S - 1);
-        const int slot_next = (kt + 1) & (S - 1);
-        const int slot_fill = (kt + S - 1) & (S - 1);   // stage kt-1's slot: free since the last barrier
+    for (int g = 0; g < steps; ++g) {
+        const int slot = g & (S - 1);
+        const int slot_next = (g + 1) & (S - 1);
+        const int slot_fill = (g + S - 1) & (S - 1);   // step g-1's slot: free since the last barrier
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int cur = ks & 1, nxt = cur ^ 1;
             const bool last = ks == NKS - 1;
             if (last) {
-                wait_vmcnt<(S - 2) * NQ>();   // stage kt+1 landed (for this wave)
+                wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
                 lds_barrier();                // ... and for every wave
             }
             // Work spread over this k-step's MFMAs: the next k-step's fragment
             // reads (from the next stage after the barrier), then, in the first
-            // k-step, the DMAs of stage kt+S-1.
+            // k-step, the DMAs of step g+S-1.
             const int n_items = NF + (ks == 0 ? NQ : 0);
 #pragma unroll
             for (int t = 0; t < NMF; ++t) {
@@ -662,22 +705,29 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                         if (last) read_unit(nxt, slot_next, 0, u);
                         else read_unit(nxt, slot, ks + 1, u);
                     } else {
-                        dma(kt + S - 1, slot_fill, u - NF);
+                        dma(slot_fill, u - NF);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (ks == 0) fill_advance();
+        }
+        if (++c_kt == KT) {
+            // Fused epilogue of the finished tile: ReLU, round to the dtype,
+            // masked store; then start the next tile from zero.
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    store_block<DT>(C, acc[i][j], lane, c_m0 + wm * WTM + j * 32, c_n0 + wn * WTN + i * 32, M, N,
+                                    c_vec_ok != 0);
+                    acc[i][j] = floatx16{0};
+                }
+            c_kt = 0;
+            if (++c_tile < n_tiles) tile_origin(c_tile, c_m0, c_n0);
         }
     }
     wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
-
-    // Fused epilogue: ReLU, round to the dtype, masked store.
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-            store_block<DT>(C, acc[i][j], lane, m0 + wm * WTM + j * 32, n0 + wn * WTN + i * 32, M, N,
-                            c_vec_ok != 0);
 }
 
 // Instances.
