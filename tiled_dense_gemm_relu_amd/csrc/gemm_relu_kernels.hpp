@@ -689,9 +689,15 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             const int cur = ks & 1, nxt = cur ^ 1;
             const bool last = ks == NKS - 1;
             if (last) {
+                __builtin_amdgcn_s_setprio(0);
                 wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
                 lds_barrier();                // ... and for every wave
             }
+            // Issue priority 1 for the first k-steps of each K-step (MFMAs and
+            // DMA issue), 0 from the barrier wait through the last k-step: of
+            // the two waves sharing a SIMD, the one further along the K-step
+            // issues first (measured: about +1%).
+            if (ks == 0) __builtin_amdgcn_s_setprio(1);
             // Work spread over this k-step's MFMAs: the next k-step's fragment
             // reads (from the next stage after the barrier), then, in the first
             // k-step, the DMAs of step g+S-1.
@@ -727,6 +733,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             if (++c_tile < n_tiles) tile_origin(c_tile, c_m0, c_n0);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
 }
 
