@@ -57,26 +57,28 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make_sets(w, n_sets, device):
+def make_sets(w, n_sets, device, b_layout=binding.B_KN):
     sets = []
     for i in range(n_sets):
         g_seed = w.seed + 1000 * i
         a, b = inputs.normal_pair(w.M, w.N, w.K, w.torch_dtype, w.scale, g_seed)
+        if b_layout == binding.B_NK:
+            b = b.t().contiguous()          # handed over as B^T, (N, K)
         c = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=device)
         sets.append((a.to(device), b.to(device), c))
     return sets
 
 
-def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO):
+def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN):
     """Returns (ms per step over the timed region, mean kernel ms from per-launch events)."""
-    sets = make_sets(w, n_sets, device)
+    sets = make_sets(w, n_sets, device, b_layout)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
 
     def launch(i):
         a, b, c = sets[i % n_sets]
         rc = binding.gemm_relu_raw(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, dt,
-                                   stream.cuda_stream, config)
+                                   stream.cuda_stream, config, b_layout)
         if rc != 0:
             raise binding.GemmReluError(rc, gr.strerror(rc))
 
@@ -151,6 +153,8 @@ def main():
     p.add_argument("--workload", default="square_8192", choices=sorted(inputs.WORKLOADS))
     p.add_argument("--sets", type=int, default=3, help="rotated input/output sets")
     p.add_argument("--config", type=int, default=binding.CONFIG_AUTO)
+    p.add_argument("--b-layout", choices=["kn", "nk"], default="kn",
+                   help="B handed over as (K, N) or as B^T, (N, K)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
@@ -173,9 +177,11 @@ def main():
     gr.load_library()
 
     w = inputs.WORKLOADS[args.workload]
-    cfg = gr.selected_config(w.M, w.N, w.K, binding.F16 if w.dtype == "fp16" else binding.BF16, args.config)
+    b_layout = binding.B_NK if args.b_layout == "nk" else binding.B_KN
+    cfg = gr.selected_config(w.M, w.N, w.K, binding.F16 if w.dtype == "fp16" else binding.BF16, args.config,
+                             b_layout=b_layout)
     log(f"[bench] {w.name}: config {cfg}")
-    ms_step, kernel_ms = time_workload(w, args.steps, args.warmup, args.sets, device, args.config)
+    ms_step, kernel_ms = time_workload(w, args.steps, args.warmup, args.sets, device, args.config, b_layout)
     tflops = w.flop / (ms_step * 1e-3) / 1e12
     kernel_tflops = w.flop / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -183,11 +189,14 @@ def main():
 
     secondary = {}
     if not args.no_secondary:
-        for name in ("square_1024", "ragged_4000x11000x4100", "skinny_64x16384x8192"):
+        for name, b_layout in (("square_1024", binding.B_KN), ("ragged_4000x11000x4100", binding.B_KN),
+                               ("skinny_64x16384x8192", binding.B_KN), ("square_8192", binding.B_NK)):
             sw = inputs.WORKLOADS[name]
-            if sw.name == w.name:
+            if sw.name == w.name and args.b_layout == ("nk" if b_layout == binding.B_NK else "kn"):
                 continue
-            s_ms, s_kms = time_workload(sw, 50, 10, 3, device)
+            s_ms, s_kms = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, b_layout=b_layout)
+            if b_layout == binding.B_NK:
+                name += "_b_nk"
             entry = {"ms": round(s_kms, 5), "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
                      "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}
@@ -218,11 +227,12 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "accumulate": "fp32",
                    "input_dist": f"N(0,1)*{w.scale}", "kernel": binding.CONFIG_NAMES.get(cfg["config_id"]),
                    "block": [cfg["block_m"], cfg["block_n"], cfg["block_k"]], "stages": cfg["stages"],
-                   "grid": cfg["grid"], "rotated_sets": args.sets},
+                   "grid": cfg["grid"], "rotated_sets": args.sets, "b_layout": args.b_layout},
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(kernel_tflops / peak, 4),
-                     "traffic": measured_traffic(w.name, binding.CONFIG_NAMES.get(cfg["config_id"]))},
+                     "traffic": (measured_traffic(w.name, binding.CONFIG_NAMES.get(cfg["config_id"]))
+                                 if b_layout == binding.B_KN else None)},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

@@ -57,7 +57,26 @@ enum {
     GEMM_RELU_ERR_NO_DEVICE = -5,   /* no current HIP device, or it is not gfx950 */
     GEMM_RELU_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
     GEMM_RELU_ERR_TOO_LARGE = -7,   /* a dimension or an addressed band exceeds the limits above */
-    GEMM_RELU_ERR_BAD_CONFIG = -8   /* an unknown kernel configuration id */
+    GEMM_RELU_ERR_BAD_CONFIG = -8,  /* an unknown kernel configuration id */
+    GEMM_RELU_ERR_BAD_LAYOUT = -9   /* b_layout is neither GEMM_RELU_B_KN nor GEMM_RELU_B_NK */
+};
+
+/* How B is stored (gemm_relu_ex).  The operation is C = ReLU(A @ B) with B of
+ * shape (K, N) either way.
+ *   GEMM_RELU_B_KN: B itself, (K, N) row-major (leading dimension N).
+ *   GEMM_RELU_B_NK: B^T, an (N, K) row-major array Bt with B[k][n] = Bt[n][k]
+ *                   (leading dimension K): the "transpose_B" GEMM, whose B
+ *                   buffer is declared (N, K) with a (block_N, block_K) shared
+ *                   tile in "TileLang Guide: Composable Tiled AI Kernel
+ *                   Programming" (aifetchly blog, sections "Tiles as
+ *                   First-Class Language Primitives" and "Step 1: Defining the
+ *                   Composable Kernel"); the tile-level gemm of "Writing
+ *                   High-Performance Kernels in TileLang" (atlascloud.ai,
+ *                   section "Let's write a GEMM", its list of primitives)
+ *                   takes the same transpose flag. */
+enum {
+    GEMM_RELU_B_KN = 0,
+    GEMM_RELU_B_NK = 1
 };
 
 /* Kernel configuration ids for gemm_relu_with_config (GEMM_RELU_CONFIG_AUTO
@@ -91,6 +110,7 @@ typedef struct {
     int64_t grid;     /* output tiles; workgroups launched, except for the DMA_* kernels, which
                          run one persistent workgroup per CU (at most one per tile) */
     int lds_bytes;    /* LDS per workgroup */
+    int b_layout;     /* GEMM_RELU_B_KN or GEMM_RELU_B_NK */
 } gemm_relu_config_t;
 
 /*
@@ -112,6 +132,26 @@ int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int6
  * error gemm_relu would return for these arguments' shape, dtype or alignment. */
 int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t M, int64_t N,
                            int64_t K, int dtype, int config_id, gemm_relu_config_t* out);
+
+/*
+ * C = ReLU(A @ B) with B stored as `b_layout` says (GEMM_RELU_B_*) and a kernel
+ * configuration (GEMM_RELU_CONFIG_*, or GEMM_RELU_CONFIG_AUTO).  With
+ * GEMM_RELU_B_KN it is gemm_relu_with_config.  With GEMM_RELU_B_NK, B points
+ * to the (N, K) array B^T; only the DMA_* and DIRECT kernels read it: a TILE_256
+ * or TILE_128 request is served by DMA_256 or DMA_128, DMA_128 and DMA_64 need
+ * K % 8 == 0 with 16-byte aligned A and B (else DMA_256 serves them), DMA_256
+ * needs K even with 4-byte aligned A and B (else DIRECT serves it).  Results,
+ * limits (B^T's 256-row band must stay below 2^31 bytes), memory, stream and
+ * error behaviour are those of gemm_relu; GEMM_RELU_ERR_BAD_LAYOUT for an
+ * unknown b_layout.
+ */
+int gemm_relu_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                 int b_layout, int config_id, void* stream);
+
+/* gemm_relu_query_config for gemm_relu_ex's arguments. */
+int gemm_relu_query_config_ex(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                              int64_t K, int dtype, int b_layout, int config_id,
+                              gemm_relu_config_t* out);
 
 /* A static, human-readable description of a return code. */
 const char* gemm_relu_strerror(int code);

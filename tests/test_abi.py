@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gemm_relu", "gemm_relu_with_config", "gemm_relu_query_config", "gemm_relu_strerror",
-        "gemm_relu_version"])
+        "gemm_relu_version", "gemm_relu_ex", "gemm_relu_query_config_ex"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -70,6 +70,17 @@ def test_invalid_arguments_are_rejected_before_launch(lib, args, code):
     a, b, c, M, N, K, dt = args
     assert lib.gemm_relu(a, b, c, M, N, K, dt, None) == code
     assert lib.gemm_relu_query_config(a, b, c, M, N, K, dt, -1, None) == code
+    # B stored (N, K) occupies the same bytes: the same checks apply
+    for b_layout in (gr.B_KN, gr.B_NK):
+        assert lib.gemm_relu_ex(a, b, c, M, N, K, dt, b_layout, -1, None) == code
+        assert lib.gemm_relu_query_config_ex(a, b, c, M, N, K, dt, b_layout, -1, None) == code
+
+
+def test_unknown_b_layout_is_rejected(lib):
+    for b_layout in (2, -1):
+        assert lib.gemm_relu_ex(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, b_layout, -1, None) == -9
+        assert lib.gemm_relu_query_config_ex(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, b_layout, -1, None) == -9
+    assert "layout" in gr.strerror(-9)
 
 
 def test_unknown_config_is_rejected(lib):
@@ -133,3 +144,40 @@ def test_dma_config_falls_back_without_suitable_loads():
 def test_direct_config_geometry():
     cfg = gr.selected_config(100, 70, 9, config=0)
     assert (cfg["block_m"], cfg["block_n"], cfg["threads"], cfg["grid"]) == (32, 32, 64, 4 * 3)
+
+
+def nt_config(M, N, K, **kw):
+    return gr.selected_config(M, N, K, b_layout=gr.B_NK, **kw)
+
+
+def test_b_nk_config_choice():
+    big = nt_config(8192, 8192, 8192)
+    assert (big["config_id"], big["vec_a"], big["vec_b"], big["b_layout"]) == (3, 8, 8, gr.B_NK)
+    assert gr.selected_config(8192, 8192, 8192)["b_layout"] == gr.B_KN
+    assert nt_config(1024, 1024, 1024)["config_id"] == 5
+    assert nt_config(2048, 2048, 2048)["config_id"] == 4
+    assert nt_config(64, 16384, 8192, dtype=gr.BF16)["config_id"] == 5
+    # B^T rows have length K: N no longer matters for the load width
+    assert nt_config(1024, 1000, 1024)["config_id"] == 5
+    assert nt_config(4000, 11003, 4096)["vec_b"] == 8
+    # K even but not a multiple of 8: the 256 kernel with 4-byte lanes for both operands
+    cfg = nt_config(1024, 1024, 1030)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
+    cfg = nt_config(8192, 8192, 8192, b_ptr=(1 << 20) + 4)           # B^T only 4-byte aligned
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
+    # odd K, or 2-byte alignment: the direct kernel
+    assert nt_config(1024, 1024, 1031)["config_id"] == 0
+    assert nt_config(8192, 8192, 8192, a_ptr=4096 + 2)["config_id"] == 0
+
+
+def test_b_nk_forced_configs():
+    # the register-staged kernels do not read B^T: TILE_* means the DMA tile of that size
+    assert nt_config(512, 512, 512, config=1)["config_id"] == 3
+    assert nt_config(512, 512, 512, config=2)["config_id"] == 4
+    for dma in (3, 4, 5):
+        assert nt_config(512, 512, 512, config=dma)["config_id"] == dma
+        assert nt_config(512, 512, 516, config=dma)["config_id"] == 3
+        assert nt_config(512, 512, 515, config=dma)["config_id"] == 0
+    assert nt_config(512, 512, 515, config=0)["config_id"] == 0
+    cfg = nt_config(512, 512, 516, config=1)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)

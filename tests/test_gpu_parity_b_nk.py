@@ -1,0 +1,141 @@
+"""GPU parity for B stored as B^T, an (N, K) row-major array (gemm_relu_ex with
+GEMM_RELU_B_NK): the "transpose_B" GEMM whose B buffer is declared (N, K) in
+"TileLang Guide: Composable Tiled AI Kernel Programming" (sections "Tiles as
+First-Class Language Primitives" and "Step 1: Defining the Composable Kernel").
+
+The oracle computes ReLU(A @ B) from B itself; the GPU is handed the bytes of
+B^T.  Bars as for the (K, N) layout: bit-exact on integer-valued inputs,
+|C_gpu - C_ref| <= 1e-2 + 1e-2 * |C_ref| on real-valued ones.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_dense_gemm_relu_amd as gr
+from tiled_dense_gemm_relu_amd import binding, inputs
+
+from test_gpu_parity import (CONFIGS, DT, assert_within_tolerance, bits, check_relu_invariants, sample_rows,
+                             say)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_nk(a, b, config=binding.CONFIG_AUTO):
+    """C = ReLU(a @ b) on the GPU, with b handed over as b^T (N, K)."""
+    bt = b.t().contiguous()
+    c = gr.gemm_relu_ex(a.cuda(), bt.cuda(), b_layout=gr.B_NK, config=config)
+    torch.cuda.synchronize()
+    return bits(c)
+
+
+NK_SHAPES = [(1, 1, 1), (33, 65, 17), (32, 32, 16), (64, 64, 8), (255, 257, 64), (256, 256, 40),
+             (300, 520, 200), (257, 263, 96), (129, 131, 200), (512, 256, 192), (64, 1000, 1024),
+             (520, 776, 1064),
+             # K even but not a multiple of 8: 4-byte DMA lanes for both operands
+             (200, 264, 100), (260, 262, 66), (300, 270, 4098)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("config", CONFIGS)
+@pytest.mark.parametrize("shape", NK_SHAPES)
+def test_b_nk_integer_inputs_bit_exact(shape, config, dtype):
+    M, N, K = shape
+    a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=3 * M + 5 * N + 11 * K)
+    want = oracle.gemm_relu(a, b, dtype)
+    assert np.array_equal(run_nk(a, b, config), want)
+
+
+@pytest.mark.parametrize("name", ["small_256", "square_1024"])
+@pytest.mark.parametrize("config", CONFIGS)
+def test_b_nk_workloads_within_tolerance(name, config):
+    w = inputs.WORKLOADS[name]
+    a, b = inputs.workload_inputs(w)
+    want = oracle.gemm_relu(a, b, w.dtype)
+    got = run_nk(a, b, config)
+    check_relu_invariants(got, w.dtype)
+    assert_within_tolerance(got, want, w.dtype)
+
+
+@pytest.mark.parametrize("config", [binding.CONFIG_DMA_256, binding.CONFIG_DMA_128, binding.CONFIG_DMA_64])
+def test_b_nk_matches_b_kn_bit_for_bit(config):
+    # Same tile, same MFMA k order: the two layouts give identical fp32 sums.
+    a, b = inputs.normal_pair(700, 520, 1000, torch.float16, 1.0, 21)
+    kn = bits(gr.gemm_relu(a.cuda(), b.cuda(), config=config))
+    torch.cuda.synchronize()
+    assert np.array_equal(run_nk(a, b, config), kn)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_b_nk_square_8192_sampled(integer):
+    w = inputs.WORKLOADS["square_8192"]
+    a, b = inputs.workload_inputs(w, integer)
+    say(f"[{w.name} B (N,K) integer={integer}] GPU run")
+    got = run_nk(a, b)
+    check_relu_invariants(got, w.dtype)
+    rows = sample_rows(w.M)
+    say(f"[{w.name} B (N,K) integer={integer}] oracle on rows {rows}")
+    want_rows = np.concatenate([oracle.gemm_relu_rows(a, b, w.dtype, r, r + 1) for r in rows])
+    rng = np.random.default_rng(w.seed + 1)
+    ii, jj = rng.integers(0, w.M, 1024), rng.integers(0, w.N, 1024)
+    want_entries = oracle.gemm_relu_entries(a, b, w.dtype, ii, jj)
+    if integer:
+        assert np.array_equal(got[rows], want_rows)
+        assert np.array_equal(got[ii, jj], want_entries)
+    else:
+        assert_within_tolerance(got[rows], want_rows, w.dtype)
+        assert_within_tolerance(got[ii, jj], want_entries, w.dtype)
+
+
+@pytest.mark.parametrize("a_off,b_off,c_off", [(1, 0, 0), (0, 1, 0), (0, 0, 1), (2, 2, 0), (4, 4, 0)])
+@pytest.mark.parametrize("config", CONFIGS)
+def test_b_nk_unaligned_pointers(a_off, b_off, c_off, config):
+    M, N, K = 130, 270, 104
+    a, b = inputs.integer_pair(M, N, K, torch.float16, seed=77)
+    want = oracle.gemm_relu(a, b, "fp16")
+    abuf = torch.zeros(M * K + a_off, dtype=torch.float16, device="cuda")
+    bbuf = torch.zeros(N * K + b_off, dtype=torch.float16, device="cuda")
+    cbuf = torch.zeros(M * N + c_off, dtype=torch.float16, device="cuda")
+    av, btv, cv = abuf[a_off:].view(M, K), bbuf[b_off:].view(N, K), cbuf[c_off:].view(M, N)
+    av.copy_(a)
+    btv.copy_(b.t())
+    gr.gemm_relu_ex(av, btv, out=cv, b_layout=gr.B_NK, config=config)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(cv), want)
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_b_nk_nothing_written_outside_c(config):
+    M, N, K = 250, 300, 72
+    guard = 4096
+    a, b = inputs.normal_pair(M, N, K, torch.bfloat16, 1.0, 6)
+    buf = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    c = buf[guard:guard + M * N].view(M, N)
+    gr.gemm_relu_ex(a.cuda(), b.t().contiguous().cuda(), out=c, b_layout=gr.B_NK, config=config)
+    torch.cuda.synchronize()
+    raw = bits(buf)
+    nan_bits = bits(torch.tensor([float("nan")], dtype=torch.bfloat16))[0]
+    assert (raw[:guard] == nan_bits).all() and (raw[guard + M * N:] == nan_bits).all()
+    assert_within_tolerance(raw[guard:guard + M * N].reshape(M, N), oracle.gemm_relu(a, b, "bf16"), "bf16")
+
+
+def test_b_nk_k_zero_and_empty():
+    a = torch.empty((37, 0), dtype=torch.float16, device="cuda")
+    bt = torch.empty((53, 0), dtype=torch.float16, device="cuda")
+    c = torch.full((37, 53), float("nan"), dtype=torch.float16, device="cuda")
+    gr.gemm_relu_ex(a, bt, out=c, b_layout=gr.B_NK)
+    torch.cuda.synchronize()
+    assert (bits(c) == 0).all()
+    assert gr.gemm_relu_ex(torch.ones((4, 16), dtype=torch.float16, device="cuda"),
+                           torch.empty((0, 16), dtype=torch.float16, device="cuda"),
+                           b_layout=gr.B_NK).shape == (4, 0)
+
+
+def test_b_nk_wrapper_checks_shapes():
+    a = torch.ones((4, 8), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        gr.gemm_relu_ex(a, torch.ones((8, 5), dtype=torch.float16, device="cuda"), b_layout=gr.B_NK)
+    with pytest.raises(ValueError):
+        gr.gemm_relu_ex(a, torch.ones((5, 8), dtype=torch.float16, device="cuda"), b_layout=7)
+    assert gr.gemm_relu_ex(a, torch.ones((5, 8), dtype=torch.float16, device="cuda"),
+                           b_layout=gr.B_NK).shape == (4, 5)

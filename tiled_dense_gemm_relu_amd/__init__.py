@@ -1,6 +1,7 @@
 """MI355X-native fused GEMM + ReLU: C = ReLU(A @ B) on gfx950 MFMA."""
 from .binding import (  # noqa: F401
     gemm_relu,
+    gemm_relu_ex,
     gemm_relu_raw,
     selected_config,
     strerror,
@@ -9,4 +10,6 @@ from .binding import (  # noqa: F401
     GemmReluError,
     F16,
     BF16,
+    B_KN,
+    B_NK,
 )

@@ -13,6 +13,10 @@ import threading
 F16 = 0
 BF16 = 1
 
+# How B is stored: (K, N) row-major, or B^T as an (N, K) row-major array.
+B_KN = 0
+B_NK = 1
+
 CONFIG_AUTO = -1
 CONFIG_DIRECT = 0
 CONFIG_TILE_256 = 1
@@ -26,7 +30,7 @@ CONFIG_NAMES = {CONFIG_DIRECT: "direct_32x32", CONFIG_TILE_256: "tile_256x256x64
 
 ERRORS = {
     0: "OK", -1: "INVALID_ARG", -2: "BAD_DTYPE", -3: "ALIAS", -4: "MISALIGNED", -5: "NO_DEVICE",
-    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG",
+    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG", -9: "BAD_LAYOUT",
 }
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +49,7 @@ class _Config(ctypes.Structure):
     _fields_ = [("config_id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("threads", ctypes.c_int),
                 ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int), ("grid", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int)]
+                ("lds_bytes", ctypes.c_int), ("b_layout", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -68,6 +72,11 @@ def load_library():
             lib.gemm_relu_with_config.restype = ci
             lib.gemm_relu_query_config.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ctypes.POINTER(_Config)]
             lib.gemm_relu_query_config.restype = ci
+            lib.gemm_relu_ex.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
+            lib.gemm_relu_ex.restype = ci
+            lib.gemm_relu_query_config_ex.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci,
+                                                      ctypes.POINTER(_Config)]
+            lib.gemm_relu_query_config_ex.restype = ci
             lib.gemm_relu_strerror.argtypes = [ci]
             lib.gemm_relu_strerror.restype = ctypes.c_char_p
             lib.gemm_relu_version.argtypes = []
@@ -86,9 +95,11 @@ def _check(code: int):
 
 
 def gemm_relu_raw(a_ptr: int, b_ptr: int, c_ptr: int, M: int, N: int, K: int, dtype: int,
-                  stream: int = 0, config: int = CONFIG_AUTO) -> int:
+                  stream: int = 0, config: int = CONFIG_AUTO, b_layout: int = B_KN) -> int:
     """Call the C ABI with raw device pointers; returns the library's status code."""
     lib = load_library()
+    if b_layout != B_KN:
+        return lib.gemm_relu_ex(a_ptr, b_ptr, c_ptr, M, N, K, dtype, b_layout, config, stream or None)
     if config == CONFIG_AUTO:
         return lib.gemm_relu(a_ptr, b_ptr, c_ptr, M, N, K, dtype, stream or None)
     return lib.gemm_relu_with_config(a_ptr, b_ptr, c_ptr, M, N, K, dtype, config, stream or None)
@@ -103,7 +114,7 @@ def _dtype_code(t) -> int:
     raise TypeError(f"gemm_relu: dtype must be float16 or bfloat16, got {t.dtype}")
 
 
-def _check_tensors(a, b, out):
+def _check_tensors(a, b, out, b_layout=B_KN):
     import torch
     for name, t in (("a", a), ("b", b)) + ((("out", out),) if out is not None else ()):
         if not isinstance(t, torch.Tensor):
@@ -116,12 +127,14 @@ def _check_tensors(a, b, out):
             raise ValueError(f"gemm_relu: {name} must be contiguous (row-major)")
     if a.dtype != b.dtype or (out is not None and out.dtype != a.dtype):
         raise TypeError("gemm_relu: a, b and out must share one dtype")
-    if a.shape[1] != b.shape[0]:
-        raise ValueError(f"gemm_relu: inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    k_b, n = (b.shape[1], b.shape[0]) if b_layout == B_NK else (b.shape[0], b.shape[1])
+    if a.shape[1] != k_b:
+        raise ValueError(f"gemm_relu: inner dimensions differ: a {tuple(a.shape)}, b {tuple(b.shape)}"
+                         f" stored {'(N, K)' if b_layout == B_NK else '(K, N)'}")
     if a.device != b.device or (out is not None and out.device != a.device):
         raise ValueError("gemm_relu: a, b and out must be on one device")
-    if out is not None and tuple(out.shape) != (a.shape[0], b.shape[1]):
-        raise ValueError(f"gemm_relu: out must have shape {(a.shape[0], b.shape[1])}, got {tuple(out.shape)}")
+    if out is not None and tuple(out.shape) != (a.shape[0], n):
+        raise ValueError(f"gemm_relu: out must have shape {(a.shape[0], n)}, got {tuple(out.shape)}")
 
 
 def gemm_relu(a, b, out=None, config: int = CONFIG_AUTO, stream=None):
@@ -130,24 +143,41 @@ def gemm_relu(a, b, out=None, config: int = CONFIG_AUTO, stream=None):
     ``out`` (M, N) is written if given, else allocated.  The kernel is enqueued
     on ``stream`` (a torch.cuda.Stream), by default torch's current stream.
     """
+    return gemm_relu_ex(a, b, out=out, b_layout=B_KN, config=config, stream=stream)
+
+
+def gemm_relu_ex(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_AUTO, stream=None):
+    """C = ReLU(a @ B) with B stored as ``b_layout`` says.
+
+    B_KN: ``b`` is B, (K, N) row-major.  B_NK: ``b`` is B^T, an (N, K)
+    row-major tensor (e.g. a weight stored output-major), so C = ReLU(a @ b.T).
+    """
     import torch
-    _check_tensors(a, b, out)
+    if b_layout not in (B_KN, B_NK):
+        raise ValueError(f"gemm_relu: b_layout must be B_KN or B_NK, got {b_layout}")
+    _check_tensors(a, b, out, b_layout)
     dtype = _dtype_code(a)
     M, K = a.shape
-    N = b.shape[1]
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
-        rc = gemm_relu_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, s.cuda_stream, config)
+        rc = gemm_relu_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, s.cuda_stream, config,
+                           b_layout)
     _check(rc)
     return out
 
 
 def selected_config(M: int, N: int, K: int, dtype: int = F16, config: int = CONFIG_AUTO,
-                    a_ptr: int = 256, b_ptr: int = 256, c_ptr: int = 1 << 40) -> dict:
+                    a_ptr: int = 256, b_ptr: int = 256, c_ptr: int = 1 << 40, b_layout: int = B_KN) -> dict:
     """The kernel configuration the library would pick (host logic only, no device needed)."""
     cfg = _Config()
-    rc = load_library().gemm_relu_query_config(a_ptr, b_ptr, c_ptr, M, N, K, dtype, config, ctypes.byref(cfg))
+    lib = load_library()
+    if b_layout == B_KN:
+        rc = lib.gemm_relu_query_config(a_ptr, b_ptr, c_ptr, M, N, K, dtype, config, ctypes.byref(cfg))
+    else:
+        rc = lib.gemm_relu_query_config_ex(a_ptr, b_ptr, c_ptr, M, N, K, dtype, b_layout, config,
+                                           ctypes.byref(cfg))
     _check(rc)
     return {f: getattr(cfg, f) for f, _ in _Config._fields_}

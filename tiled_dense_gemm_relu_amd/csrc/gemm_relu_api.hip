@@ -12,7 +12,7 @@
 namespace gemm_relu_hip {
 namespace {
 
-constexpr int kVersion = 100;                    // 0.1.0
+constexpr int kVersion = 200;                    // 0.2.0
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 22;
 constexpr int64_t kMaxBand = (int64_t(1) << 31) - 1;   // bytes one buffer descriptor may address
@@ -23,6 +23,7 @@ struct Plan {
     int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 an LDS-DMA kernel (dma_id)
     int dma_id;        // DmaId when tile == -4
     int dma_a4, dma_b4;    // 4-byte DMA lanes for A / B (256 LDS-DMA kernel only)
+    int b_nk;          // B given as (N, K)
     int vec_pair;      // index into kVecPairs
     int tiles_m, tiles_n;
     int c_vec_ok;
@@ -49,9 +50,10 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes)
 
 // Every check that needs no device.  Fills `plan` on success.
 int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K, int dtype,
-              int config_id, Plan* plan)
+              int b_layout, int config_id, Plan* plan)
 {
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
+    if (b_layout != GEMM_RELU_B_KN && b_layout != GEMM_RELU_B_NK) return GEMM_RELU_ERR_BAD_LAYOUT;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
     if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_64)
         return GEMM_RELU_ERR_BAD_CONFIG;
@@ -59,6 +61,8 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 
     std::memset(plan, 0, sizeof(*plan));
     plan->cfg.config_id = config_id;
+    plan->cfg.b_layout = b_layout;
+    plan->b_nk = b_layout == GEMM_RELU_B_NK ? 1 : 0;
     plan->tile = -3;
     if (M == 0 || N == 0) return GEMM_RELU_OK;        // nothing to compute or write
 
@@ -84,11 +88,29 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         return GEMM_RELU_OK;
     }
 
-    const int va = vec_width(A, K), vb = vec_width(B, N);
+    const int va = vec_width(A, K), vb = vec_width(B, plan->b_nk ? K : N);
     const bool full_vectors = va == 8 && vb == 8;
     // 4-byte DMA lanes work for rows of an even length with 4-byte aligned bases.
     const bool dword_vectors = va >= 2 && vb >= 2;
     int chosen = config_id;
+    if (plan->b_nk) {
+        // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
+        // operands, or 4-byte lanes for both in the 256 one) and the direct
+        // kernel read it.  A TILE_* request means the DMA tile of its size.
+        if (chosen == GEMM_RELU_CONFIG_AUTO) {
+            const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+            const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
+            if (t256 >= 192 || (!full_vectors && dword_vectors))
+                chosen = GEMM_RELU_CONFIG_DMA_256;
+            else
+                chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_64;
+        }
+        if (chosen == GEMM_RELU_CONFIG_TILE_256) chosen = GEMM_RELU_CONFIG_DMA_256;
+        if (chosen == GEMM_RELU_CONFIG_TILE_128) chosen = GEMM_RELU_CONFIG_DMA_128;
+        if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64) && !full_vectors)
+            chosen = GEMM_RELU_CONFIG_DMA_256;
+        if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_DIRECT;
+    }
     if (chosen == GEMM_RELU_CONFIG_AUTO) {
         // The largest tile that still yields enough workgroups to cover the 256
         // CUs (192+ tiles); LDS-DMA kernels when 16-byte loads are possible (the
@@ -110,7 +132,8 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     if (chosen >= GEMM_RELU_CONFIG_DMA_256) {
         const int id = chosen - GEMM_RELU_CONFIG_DMA_256;
         const TileGeom& g = kDmaGeom[id];
-        if (int64_t(g.bm) * K * 2 > kMaxBand || int64_t(g.bk) * N * 2 > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
+        const int64_t b_band = plan->b_nk ? int64_t(g.bn) * K * 2 : int64_t(g.bk) * N * 2;
+        if (int64_t(g.bm) * K * 2 > kMaxBand || b_band > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
         const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
         if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
         plan->tile = -4;
@@ -124,8 +147,9 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         plan->cfg.threads = g.threads;
         plan->dma_a4 = va < 8 ? 1 : 0;     // only the 256 kernel gets here with va or vb < 8
         plan->dma_b4 = vb < 8 ? 1 : 0;
-        plan->cfg.vec_a = va < 8 ? 2 : 8;
-        plan->cfg.vec_b = vb < 8 ? 2 : 8;
+        if (plan->b_nk) plan->dma_a4 = plan->dma_b4 = full_vectors ? 0 : 1;   // one lane width for both
+        plan->cfg.vec_a = plan->dma_a4 ? 2 : 8;
+        plan->cfg.vec_b = plan->dma_b4 ? 2 : 8;
         plan->cfg.grid = tm * tn;
         plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2;
         return GEMM_RELU_OK;
@@ -211,12 +235,14 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
     } else if (p.tile == -1) {
         int tiles_m = p.tiles_m, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &c_vec_ok};
-        err = hipLaunchKernel(ks.direct, dim3((unsigned)p.cfg.grid), dim3(64), args, 0, stream);
+        err = hipLaunchKernel(p.b_nk ? ks.direct_nt : ks.direct, dim3((unsigned)p.cfg.grid), dim3(64), args, 0,
+                              stream);
     } else {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
         const int ktail = p.tile == -4 && K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0;
         const void* fn = p.tile != -4 ? ks.tiled[p.tile][p.vec_pair]
+                       : p.b_nk ? (p.dma_id == kDma256 && p.dma_a4 ? ks.dma256_nt_dw[ktail] : ks.dma_nt[p.dma_id][ktail])
                        : p.dma_id == kDma256 ? ks.dma256_dw[p.dma_a4][p.dma_b4][ktail]
                                              : ks.dma[p.dma_id][ktail];
         // The LDS-DMA kernels are persistent: one workgroup per CU (their LDS
@@ -234,20 +260,26 @@ using namespace gemm_relu_hip;
 
 extern "C" {
 
-int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
-                           int dtype, int config_id, gemm_relu_config_t* out)
+int gemm_relu_query_config_ex(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                              int dtype, int b_layout, int config_id, gemm_relu_config_t* out)
 {
     Plan p;
-    const int rc = make_plan(A, B, C, M, N, K, dtype, config_id, &p);
+    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, &p);
     if (rc == GEMM_RELU_OK && out) *out = p.cfg;
     return rc;
 }
 
-int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
-                          int config_id, void* stream)
+int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                           int dtype, int config_id, gemm_relu_config_t* out)
+{
+    return gemm_relu_query_config_ex(A, B, C, M, N, K, dtype, GEMM_RELU_B_KN, config_id, out);
+}
+
+int gemm_relu_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                 int config_id, void* stream)
 {
     Plan p;
-    int rc = make_plan(A, B, C, M, N, K, dtype, config_id, &p);
+    int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, &p);
     if (rc != GEMM_RELU_OK) return rc;
     if (p.tile == -3) return GEMM_RELU_OK;          // M == 0 or N == 0
     int cus = 0;
@@ -256,9 +288,15 @@ int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int6
     return launch(p, A, B, C, M, N, K, dtype, cus, static_cast<hipStream_t>(stream));
 }
 
+int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                          int config_id, void* stream)
+{
+    return gemm_relu_ex(A, B, C, M, N, K, dtype, GEMM_RELU_B_KN, config_id, stream);
+}
+
 int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype, void* stream)
 {
-    return gemm_relu_with_config(A, B, C, M, N, K, dtype, GEMM_RELU_CONFIG_AUTO, stream);
+    return gemm_relu_ex(A, B, C, M, N, K, dtype, GEMM_RELU_B_KN, GEMM_RELU_CONFIG_AUTO, stream);
 }
 
 const char* gemm_relu_strerror(int code)
@@ -273,6 +311,7 @@ const char* gemm_relu_strerror(int code)
     case GEMM_RELU_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_RELU_ERR_TOO_LARGE: return "dimensions exceed the supported range";
     case GEMM_RELU_ERR_BAD_CONFIG: return "unknown kernel configuration id";
+    case GEMM_RELU_ERR_BAD_LAYOUT: return "unknown B layout (expected GEMM_RELU_B_KN or GEMM_RELU_B_NK)";
     default: return "unknown error code";
     }
 }

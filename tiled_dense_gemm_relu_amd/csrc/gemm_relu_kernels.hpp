@@ -475,15 +475,18 @@ __device__ __forceinline__ int b_swizzle(int k)
 }
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_,
-          int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16>
+          int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16, bool B_KMAJOR_ = false>
 struct DmaConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, GROUP_M = GROUP_M_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;     // wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;               // 32x32 MFMA blocks per wave
     static constexpr int NKS = BK / 16;                              // MFMA k-steps per stage
-    static constexpr int A_ROW = BK * 2, B_ROW = BN * 2;             // bytes per LDS row
-    static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BK * B_ROW; // bytes per stage
+    // B_KMAJOR: B is given as B^T, an (N, K) row-major array, so its LDS stage
+    // has A's shape (BN rows of BK k) and its fragments are plain ds_read_b128.
+    static constexpr bool B_KMAJOR = B_KMAJOR_;
+    static constexpr int A_ROW = BK * 2, B_ROW = B_KMAJOR ? BK * 2 : BN * 2;   // bytes per LDS row
+    static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * BK * 2;          // bytes per stage
     static constexpr int B_REGION = STAGES * A_STAGE;                // B stages follow the A stages
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
     // Bytes each lane moves per DMA instruction: 16 (buffer_load_dwordx4, needs
@@ -563,22 +566,33 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     for (int q = 0; q < QB; ++q) {
         const int byte = ((wave * QB + q) * 64 + lane) * LB;       // offset inside the B stage
         const int row = byte / B_ROW;
-        const int lc = ((byte % B_ROW) / 16) ^ b_swizzle<B_ROW>(row);
-        const int ncol = lc * 8 + (byte % 16) / 2;                  // first n of this lane's piece, from n0
-        b_voff[q] = (uint32_t)row * (uint32_t)N * 2u + (uint32_t)ncol * 2u;
-        b_ncol[q] = ncol;
+        if constexpr (Cfg::B_KMAJOR) {                              // row = n, K-contiguous like A
+            const int lc = ((byte % B_ROW) / 16) ^ a_swizzle<B_ROW>(row);
+            const int kcol = lc * 8 + (byte % 16) / 2;
+            b_voff[q] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)kcol * 2u;
+            b_ncol[q] = kcol;                                       // here: first k of the piece
+        } else {                                                    // row = k, N-contiguous
+            const int lc = ((byte % B_ROW) / 16) ^ b_swizzle<B_ROW>(row);
+            const int ncol = lc * 8 + (byte % 16) / 2;              // first n of this lane's piece, from n0
+            b_voff[q] = (uint32_t)row * (uint32_t)N * 2u + (uint32_t)ncol * 2u;
+            b_ncol[q] = ncol;
+        }
     }
     const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
 
     // The load side of the stream: the tile and K-step the next DMA belongs to.
     int f_tile = 0, f_kt = 0, f_m0 = 0, f_n0 = 0;
-    int32x4_t f_rsrc_a = rsrc_none;
+    int32x4_t f_rsrc_a = rsrc_none, f_rsrc_bt = rsrc_none;
     auto fill_tile_setup = [&]() {
         if (f_tile < n_tiles) {
             tile_origin(f_tile, f_m0, f_n0);
             // rows f_m0 .. f_m0 + valid_m - 1 of A; rows past M read as zero
             const int valid_m = min(BM, M - f_m0);
             f_rsrc_a = rsrc_words(A + (size_t)f_m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
+            if constexpr (Cfg::B_KMAJOR) {   // rows f_n0 .. of B^T; rows past N read as zero
+                const int valid_n = min(BN, N - f_n0);
+                f_rsrc_bt = rsrc_words(B + (size_t)f_n0 * (size_t)K, (uint32_t)valid_n * (uint32_t)K * 2u);
+            }
         }
     };
     fill_tile_setup();
@@ -601,6 +615,15 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             }
             dma_issue(live ? f_rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 64 * LA, vo,
                       live ? so : 0u, LA);
+        } else if constexpr (Cfg::B_KMAJOR) {
+            const int qb = q - QA;
+            uint32_t vo = b_voff[qb], so = (uint32_t)k0 * 2u;
+            if (KTAIL) {
+                vo = k0 + b_ncol[qb] < K ? b_voff[qb] + so : kOobOffset;
+                so = 0u;
+            }
+            dma_issue(live ? f_rsrc_bt : rsrc_none, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + qb) * 64 * LB,
+                      vo, live ? so : 0u, LB);
         } else {
             // descriptor based at (row k0, column f_n0): rows past K read as zero
             const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
@@ -629,8 +652,15 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     }
     //  B^T fragment i, k-step ks, half hh: lane group g = lane/16, j = lane%16;
     //  row k = 16ks + 8(g/2) + 4hh + j/4, column n = wn*WTN + 32i + 16(g%2) + 4(j%4).
-    uint32_t b_frag_off[FN];
-    {
+    //  (B_KMAJOR: like A, row n = wn*WTN + 32i + lane%32, chunk 2ks + lane/32.)
+    uint32_t b_frag_off[Cfg::B_KMAJOR ? NKS : FN];
+    if constexpr (Cfg::B_KMAJOR) {
+        const int row = wn * WTN + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            b_frag_off[ks] = (uint32_t)(Cfg::B_REGION + row * B_ROW +
+                                        16 * ((2 * ks + (lane >> 5)) ^ a_swizzle<B_ROW>(row)));
+    } else {
         const int g = lane >> 4, j = lane & 15;
         const int krow = 8 * (g >> 1) + (j >> 2);          // + 16ks + 4hh leave the swizzle unchanged
 #pragma unroll
@@ -653,10 +683,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         fb[buf][j] = *reinterpret_cast<const u32x4*>(smem + slot * Cfg::A_STAGE + a_frag_off[ks] + j * 32 * A_ROW);
     };
     auto read_b = [&](int buf, int slot, int ks, int i) {
-        const uint8_t* p = smem + slot * Cfg::B_STAGE + b_frag_off[i] + 16 * ks * B_ROW;
-        const u32x2 lo = ds_read_tr16(p);
-        const u32x2 hi = ds_read_tr16(p + 4 * B_ROW);
-        fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        if constexpr (Cfg::B_KMAJOR) {
+            fa[buf][i] = *reinterpret_cast<const u32x4*>(smem + slot * Cfg::B_STAGE + b_frag_off[ks] + i * 32 * B_ROW);
+        } else {
+            const uint8_t* p = smem + slot * Cfg::B_STAGE + b_frag_off[i] + 16 * ks * B_ROW;
+            const u32x2 lo = ds_read_tr16(p);
+            const u32x2 hi = ds_read_tr16(p + 4 * B_ROW);
+            fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
     };
     auto read_unit = [&](int buf, int slot, int ks, int u) {
         if (u < FM) read_a(buf, slot, ks, u);
@@ -744,6 +778,11 @@ using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;   // ... with B
 using DmaTile256AB4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4>;   // ... both
 using DmaTile128 = DmaConfig<128, 128, 64, 4, 2, 2, 4>;   // mid shapes: 4 waves of 64x64
 using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny shapes: 4 waves of 32x32, 8 stages
+// B given as B^T, (N, K) row-major
+using DmaTile256T = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 16, true>;
+using DmaTile256T4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4, true>;    // K even but not a multiple of 8
+using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
+using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
 
 // ---------------------------------------------------------------- direct kernel
 
@@ -751,7 +790,8 @@ using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny sh
 // with a bounds check per element.  No LDS, no alignment requirement beyond
 // 2 bytes.  It is the general path for shapes the tiled kernels cannot take
 // and a second, structurally different GPU implementation for the tests.
-template <int DT>
+// B_NK: B is given as B^T, an (N, K) row-major array.
+template <int DT, bool B_NK = false>
 __global__ __launch_bounds__(64) void gemm_relu_direct(const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ B,
                                                        uint16_t* __restrict__ C, int M, int N, int K,
@@ -770,8 +810,13 @@ __global__ __launch_bounds__(64) void gemm_relu_direct(const uint16_t* __restric
         for (int p = 0; p < 4; ++p) {
             uint32_t lo_a = 0, hi_a = 0, lo_b = 0, hi_b = 0;
             const int k = k0 + kg + 2 * p;
-            if (n < N && k < K) lo_a = B[(size_t)k * N + n];
-            if (n < N && k + 1 < K) hi_a = B[(size_t)(k + 1) * N + n];
+            if (B_NK) {
+                if (n < N && k < K) lo_a = B[(size_t)n * K + k];
+                if (n < N && k + 1 < K) hi_a = B[(size_t)n * K + k + 1];
+            } else {
+                if (n < N && k < K) lo_a = B[(size_t)k * N + n];
+                if (n < N && k + 1 < K) hi_a = B[(size_t)(k + 1) * N + n];
+            }
             if (m < M && k < K) lo_b = A[(size_t)m * K + k];
             if (m < M && k + 1 < K) hi_b = A[(size_t)m * K + k + 1];
             fa[p] = lo_a | (hi_a << 16);

@@ -28,6 +28,12 @@ struct DtypeKernels {
     // The 256 LDS-DMA kernel with 4-byte DMA lanes: [A 4-byte][B 4-byte][K % BK != 0]
     // (index [0][0] unused: that is dma[kDma256]); need 2-element loads.
     const void* dma256_dw[2][2][2];
+    // B given as B^T, an (N, K) row-major array: the direct kernel, the
+    // LDS-DMA kernels with 16-byte lanes by DmaId and [K % BK != 0], and the
+    // 256 one with 4-byte lanes by [K % BK != 0].
+    const void* direct_nt;
+    const void* dma_nt[3][2];
+    const void* dma256_nt_dw[2];
 };
 
 // LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.

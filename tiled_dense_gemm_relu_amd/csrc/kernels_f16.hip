@@ -19,7 +19,9 @@ constexpr bool dma_geom_matches = Cfg::BM == kDmaGeom[id].bm && Cfg::BN == kDmaG
                                   Cfg::BK == kDmaGeom[id].bk && Cfg::STAGES == kDmaGeom[id].stages &&
                                   Cfg::THREADS == kDmaGeom[id].threads && Cfg::GROUP_M == kDmaGeom[id].group_m;
 static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
-                  dma_geom_matches<DmaTile64, kDma64>,
+                  dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
+                  dma_geom_matches<DmaTile256T4, kDma256> && dma_geom_matches<DmaTile128T, kDma128> &&
+                  dma_geom_matches<DmaTile64T, kDma64>,
               "host DMA tile geometry out of date");
 
 template <class Cfg>
@@ -53,6 +55,15 @@ DtypeKernels make_table()
     t.dma256_dw[0][1][1] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, true>;
     t.dma256_dw[1][1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, false>;
     t.dma256_dw[1][1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, true>;
+    t.direct_nt = (const void*)&gemm_relu_direct<kF16, true>;
+    t.dma_nt[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256T, kF16, false>;
+    t.dma_nt[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256T, kF16, true>;
+    t.dma_nt[kDma128][0] = (const void*)&gemm_relu_dma<DmaTile128T, kF16, false>;
+    t.dma_nt[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128T, kF16, true>;
+    t.dma_nt[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64T, kF16, false>;
+    t.dma_nt[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64T, kF16, true>;
+    t.dma256_nt_dw[0] = (const void*)&gemm_relu_dma<DmaTile256T4, kF16, false>;
+    t.dma256_nt_dw[1] = (const void*)&gemm_relu_dma<DmaTile256T4, kF16, true>;
     return t;
 }
 }  // namespace
