@@ -69,16 +69,31 @@ def make_sets(w, n_sets, device, b_layout=binding.B_KN):
     return sets
 
 
-def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN):
-    """Returns (ms per step over the timed region, mean kernel ms from per-launch events)."""
+def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN,
+                  splits=None):
+    """Returns (ms per step over the timed region, mean kernel ms from per-launch events).
+    splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with that many parts."""
     sets = make_sets(w, n_sets, device, b_layout)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
+    lib = gr.load_library()
+    ws, ws_bytes = None, 0
+    if splits is not None:
+        cfg = gr.selected_splitk_config(w.M, w.N, w.K, dt, config, splits, b_layout=b_layout)
+        log(f"[bench] {w.name} split-K: {cfg}")
+        if cfg["workspace_bytes"]:
+            ws = binding.splitk_workspace(device, stream, cfg["workspace_bytes"])
+            ws_bytes = ws.numel()
 
     def launch(i):
         a, b, c = sets[i % n_sets]
-        rc = binding.gemm_relu_raw(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, dt,
-                                   stream.cuda_stream, config, b_layout)
+        if splits is None:
+            rc = binding.gemm_relu_raw(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, dt,
+                                       stream.cuda_stream, config, b_layout)
+        else:
+            rc = lib.gemm_relu_splitk(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, dt, b_layout,
+                                      config, splits, ws.data_ptr() if ws is not None else None, ws_bytes,
+                                      stream.cuda_stream or None)
         if rc != 0:
             raise binding.GemmReluError(rc, gr.strerror(rc))
 
@@ -189,14 +204,26 @@ def main():
 
     secondary = {}
     if not args.no_secondary:
-        for name, b_layout in (("square_1024", binding.B_KN), ("ragged_4000x11000x4100", binding.B_KN),
-                               ("skinny_64x16384x8192", binding.B_KN), ("square_8192", binding.B_NK)):
+        # (workload, B layout, kernel config, split-K parts or None for the plain entry point)
+        runs = [("square_1024", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, 4),
+                ("ragged_4000x11000x4100", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, 0),
+                ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
+                ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None)]
+        for name, b_layout, s_config, s_splits in runs:
             sw = inputs.WORKLOADS[name]
-            if sw.name == w.name and args.b_layout == ("nk" if b_layout == binding.B_NK else "kn"):
+            if (sw.name == w.name and s_splits is None and
+                    args.b_layout == ("nk" if b_layout == binding.B_NK else "kn")):
                 continue
-            s_ms, s_kms = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, b_layout=b_layout)
+            s_ms, s_kms = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, config=s_config,
+                                        b_layout=b_layout, splits=s_splits)
             if b_layout == binding.B_NK:
                 name += "_b_nk"
+            if s_splits is not None:
+                name += "_splitk" if s_config == binding.CONFIG_AUTO else f"_splitk{s_splits}_config{s_config}"
             entry = {"ms": round(s_kms, 5), "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
                      "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}

@@ -15,8 +15,9 @@
  * allocates C itself and passes it in; this ABI does the same.
  *
  * Memory: A, B and C are device pointers owned by the caller (e.g. torch
- * allocations).  The library allocates nothing per call and keeps no state
- * between calls except a per-device cache of the device's architecture.
+ * allocations).  The library allocates nothing and keeps no state between
+ * calls except a per-device cache of the device's architecture (split-K takes
+ * a caller-owned workspace).
  *
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL means the null
  * stream) and the call returns without waiting.  C is complete once the
@@ -58,7 +59,8 @@ enum {
     GEMM_RELU_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
     GEMM_RELU_ERR_TOO_LARGE = -7,   /* a dimension or an addressed band exceeds the limits above */
     GEMM_RELU_ERR_BAD_CONFIG = -8,  /* an unknown kernel configuration id */
-    GEMM_RELU_ERR_BAD_LAYOUT = -9   /* b_layout is neither GEMM_RELU_B_KN nor GEMM_RELU_B_NK */
+    GEMM_RELU_ERR_BAD_LAYOUT = -9,  /* b_layout is neither GEMM_RELU_B_KN nor GEMM_RELU_B_NK */
+    GEMM_RELU_ERR_WORKSPACE = -10   /* split-K workspace missing, too small or not 256-byte aligned */
 };
 
 /* How B is stored (gemm_relu_ex).  The operation is C = ReLU(A @ B) with B of
@@ -89,12 +91,14 @@ enum {
     GEMM_RELU_CONFIG_DMA_256 = 3,     /* 256x256x32 block tile, 8 waves, 4 LDS stages filled by
                                          direct-to-LDS loads */
     GEMM_RELU_CONFIG_DMA_128 = 4,     /* 128x128x64 block tile, 4 waves, 4 direct-to-LDS stages */
-    GEMM_RELU_CONFIG_DMA_64 = 5       /* 64x64x64 block tile, 4 waves, 8 direct-to-LDS stages
+    GEMM_RELU_CONFIG_DMA_64 = 5,      /* 64x64x64 block tile, 4 waves, 8 direct-to-LDS stages
                                          (small, skinny and bandwidth-bound shapes) */
-    /* DMA_128 and DMA_64 need 16-byte loads of A and B (K % 8 == 0, N % 8 == 0, 16-byte
-       aligned A and B); DMA_256 also takes 4-byte loads (K and N even, 4-byte aligned A and B).
-       For other inputs a DMA_* request falls back to TILE_256 (DMA_256) or TILE_128
-       (DMA_128, DMA_64). */
+    GEMM_RELU_CONFIG_DMA_64x256 = 6   /* 64x256x32 block tile, 4 waves, 8 direct-to-LDS stages
+                                         (few rows, many columns; meant for split-K) */
+    /* DMA_128, DMA_64 and DMA_64x256 need 16-byte loads of A and B (K % 8 == 0, N % 8 == 0,
+       16-byte aligned A and B); DMA_256 also takes 4-byte loads (K and N even, 4-byte aligned
+       A and B).  For other inputs a DMA_* request falls back to TILE_256 (DMA_256) or TILE_128
+       (DMA_128, DMA_64, DMA_64x256). */
 };
 
 /* What a configuration is, for reports and tests. */
@@ -111,6 +115,8 @@ typedef struct {
                          run one persistent workgroup per CU (at most one per tile) */
     int lds_bytes;    /* LDS per workgroup */
     int b_layout;     /* GEMM_RELU_B_KN or GEMM_RELU_B_NK */
+    int splits;       /* K parts per output tile (1: no split-K) */
+    int64_t workspace_bytes;   /* split-K workspace needed (0 when splits == 1) */
 } gemm_relu_config_t;
 
 /*
@@ -152,6 +158,51 @@ int gemm_relu_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, in
 int gemm_relu_query_config_ex(const void* A, const void* B, const void* C, int64_t M, int64_t N,
                               int64_t K, int dtype, int b_layout, int config_id,
                               gemm_relu_config_t* out);
+
+/*
+ * Split-K: C = ReLU(A @ B) with the K range of every output tile cut into
+ * `splits` contiguous parts that run as separate work units, for shapes with
+ * too few output tiles to occupy every CU (a few rows and many columns, or
+ * small squares).  The split-K idea is the GEMM analogue of the split/combine
+ * decode of "Writing High-Performance Kernels in TileLang" (atlascloud.ai,
+ * its MLA decode section: a num_split parameter and a combine step); ReLU is
+ * applied once, after the parts are summed, because it does not distribute
+ * over a sum.
+ *
+ * Each part accumulates its K range in fp32; the last part of a tile to finish
+ * (decided per wave sub-tile, without any waiting) adds the others' fp32
+ * partial tiles in part order (part 0 first), applies ReLU, rounds and stores C.  The sum order is fixed, so results are the same
+ * run to run; on integer-valued inputs they equal gemm_relu's bit for bit, on
+ * real-valued inputs they differ from it only by fp32 summation order.
+ *
+ * splits: 0 lets the library choose (enough parts for about 256 work units
+ * when the tiles alone are fewer than 192, else 1); n >= 1 asks for n parts.
+ * Either is capped at the tile's number of K-steps and at 64.  Only the
+ * DMA_128, DMA_64 and DMA_64x256 kernels split; with other configurations, or
+ * when the count resolves to 1, the call is gemm_relu_ex (workspace unused, may
+ * be NULL).  With GEMM_RELU_CONFIG_AUTO and M <= 64 the DMA_64x256 tile is
+ * chosen when its loads are possible.
+ *
+ * workspace: device memory of at least gemm_relu_config_t.workspace_bytes
+ * (from gemm_relu_query_splitk with the same arguments), 256-byte aligned,
+ * owned by the caller, not overlapping A, B or C.  Its first 64 KiB hold int
+ * counters (one per output tile and wave; shapes that would need more do not
+ * split), the fp32 partial tiles follow.  The counter region must be zero
+ * before the first use; every call that runs to completion leaves it at zero
+ * again, so the same workspace serves later calls of any shape without
+ * clearing.  Calls that may overlap in time (different streams) need different
+ * workspaces.
+ * Errors as gemm_relu_ex, plus GEMM_RELU_ERR_WORKSPACE, and
+ * GEMM_RELU_ERR_INVALID_ARG for splits < 0 or > 64.
+ */
+int gemm_relu_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                     int b_layout, int config_id, int splits, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/* The configuration gemm_relu_splitk would use (pure host logic), including
+ * `splits` and `workspace_bytes`.  `out` may be NULL. */
+int gemm_relu_query_splitk(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                           int dtype, int b_layout, int config_id, int splits, gemm_relu_config_t* out);
 
 /* A static, human-readable description of a return code. */
 const char* gemm_relu_strerror(int code);

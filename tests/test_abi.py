@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gemm_relu", "gemm_relu_with_config", "gemm_relu_query_config", "gemm_relu_strerror",
-        "gemm_relu_version", "gemm_relu_ex", "gemm_relu_query_config_ex"])
+        "gemm_relu_version", "gemm_relu_ex", "gemm_relu_query_config_ex", "gemm_relu_splitk",
+        "gemm_relu_query_splitk"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -84,7 +85,7 @@ def test_unknown_b_layout_is_rejected(lib):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 6, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 7, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -181,3 +182,39 @@ def test_b_nk_forced_configs():
     assert nt_config(512, 512, 515, config=0)["config_id"] == 0
     cfg = nt_config(512, 512, 516, config=1)
     assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
+
+
+def test_splitk_config_choice():
+    skinny = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16)
+    assert (skinny["config_id"], skinny["splits"], skinny["grid"]) == (6, 4, 256)
+    # the fixed 64 KiB counter region + 4 fp32 partial tiles per tile
+    assert skinny["workspace_bytes"] == 65536 + 64 * 4 * 64 * 256 * 4
+    # enough tiles already: no split, no workspace
+    big = gr.selected_splitk_config(8192, 8192, 8192)
+    assert (big["config_id"], big["splits"], big["workspace_bytes"]) == (3, 1, 0)
+    # explicit parts, capped by the K-steps
+    cfg = gr.selected_splitk_config(1024, 1024, 1024, config=4, splits=4)
+    assert (cfg["splits"], cfg["grid"]) == (4, 256)
+    assert gr.selected_splitk_config(128, 128, 128, config=4, splits=8)["splits"] == 2
+    assert gr.selected_splitk_config(1024, 1024, 1024, config=4, splits=64)["splits"] == 16
+    # the 256 tile and the register-staged kernels do not split
+    assert gr.selected_splitk_config(512, 512, 512, config=3, splits=4)["splits"] == 1
+    assert gr.selected_splitk_config(64, 512, 514, splits=4)["splits"] == 1          # K % 8 != 0
+    # more tiles than the counter region holds (16384 counters, 4 waves per tile): no split
+    assert gr.selected_splitk_config(64 * 4097, 64, 1024, config=5, splits=2)["splits"] == 1
+    assert gr.selected_splitk_config(64 * 4096, 64, 1024, config=5, splits=2)["splits"] == 2
+    # the plain entry points never split
+    assert gr.selected_config(64, 16384, 8192)["splits"] == 1
+
+
+def test_splitk_argument_errors(lib):
+    args = (A_PTR, B_PTR, C_PTR, 64, 512, 512, 0, 0, -1)
+    assert lib.gemm_relu_query_splitk(*args, -1, None) == -1
+    assert lib.gemm_relu_query_splitk(*args, 65, None) == -1
+    assert lib.gemm_relu_splitk(*args, 4, None, 0, None) == -10                   # no workspace
+    need = gr.selected_splitk_config(64, 512, 512, splits=4)["workspace_bytes"]
+    ws = 5 << 32
+    assert lib.gemm_relu_splitk(*args, 4, ws, need - 1, None) == -10              # too small
+    assert lib.gemm_relu_splitk(*args, 4, ws + 16, need, None) == -10             # misaligned
+    assert lib.gemm_relu_splitk(*args, 4, C_PTR, need, None) == -3                # overlaps C
+    assert lib.gemm_relu_splitk(A_PTR, B_PTR, C_PTR, 64, 512, 512, 0, 2, -1, 4, ws, need, None) == -9

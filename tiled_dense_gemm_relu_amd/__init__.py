@@ -2,6 +2,8 @@
 from .binding import (  # noqa: F401
     gemm_relu,
     gemm_relu_ex,
+    gemm_relu_splitk,
+    selected_splitk_config,
     gemm_relu_raw,
     selected_config,
     strerror,

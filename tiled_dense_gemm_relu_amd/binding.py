@@ -24,13 +24,15 @@ CONFIG_TILE_128 = 2
 CONFIG_DMA_256 = 3
 CONFIG_DMA_128 = 4
 CONFIG_DMA_64 = 5
+CONFIG_DMA_64x256 = 6
 CONFIG_NAMES = {CONFIG_DIRECT: "direct_32x32", CONFIG_TILE_256: "tile_256x256x64",
                 CONFIG_TILE_128: "tile_128x128x64", CONFIG_DMA_256: "dma_256x256x32_4stage",
-                CONFIG_DMA_128: "dma_128x128x64_4stage", CONFIG_DMA_64: "dma_64x64x64_8stage"}
+                CONFIG_DMA_128: "dma_128x128x64_4stage", CONFIG_DMA_64: "dma_64x64x64_8stage",
+                CONFIG_DMA_64x256: "dma_64x256x32_8stage"}
 
 ERRORS = {
     0: "OK", -1: "INVALID_ARG", -2: "BAD_DTYPE", -3: "ALIAS", -4: "MISALIGNED", -5: "NO_DEVICE",
-    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG", -9: "BAD_LAYOUT",
+    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG", -9: "BAD_LAYOUT", -10: "WORKSPACE",
 }
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -49,7 +51,8 @@ class _Config(ctypes.Structure):
     _fields_ = [("config_id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("block_k", ctypes.c_int), ("stages", ctypes.c_int), ("threads", ctypes.c_int),
                 ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int), ("grid", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int), ("b_layout", ctypes.c_int)]
+                ("lds_bytes", ctypes.c_int), ("b_layout", ctypes.c_int), ("splits", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -77,6 +80,11 @@ def load_library():
             lib.gemm_relu_query_config_ex.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci,
                                                       ctypes.POINTER(_Config)]
             lib.gemm_relu_query_config_ex.restype = ci
+            lib.gemm_relu_splitk.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, vp, i64, vp]
+            lib.gemm_relu_splitk.restype = ci
+            lib.gemm_relu_query_splitk.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci,
+                                                   ctypes.POINTER(_Config)]
+            lib.gemm_relu_query_splitk.restype = ci
             lib.gemm_relu_strerror.argtypes = [ci]
             lib.gemm_relu_strerror.restype = ctypes.c_char_p
             lib.gemm_relu_version.argtypes = []
@@ -167,6 +175,66 @@ def gemm_relu_ex(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_AUTO
                            b_layout)
     _check(rc)
     return out
+
+
+_workspaces = {}
+
+
+def splitk_workspace(device, stream, nbytes: int):
+    """A zero-filled workspace of at least ``nbytes`` for split-K calls on ``stream``.
+
+    One buffer per (device, stream), grown when needed and kept for later calls:
+    the library leaves its counters at zero after every completed call.  Calls
+    on one stream are ordered, so they may share it; other streams get their own.
+    """
+    import torch
+    key = (device, stream.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def gemm_relu_splitk(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_AUTO, splits: int = 0,
+                     workspace=None, stream=None):
+    """C = ReLU(a @ B) with each output tile's K range split into ``splits`` parts (0: the library
+    chooses).  ``workspace``: a zero-filled uint8 GPU tensor of at least the queried size, or None
+    for a cached one per stream.  B as for gemm_relu_ex."""
+    import torch
+    if b_layout not in (B_KN, B_NK):
+        raise ValueError(f"gemm_relu: b_layout must be B_KN or B_NK, got {b_layout}")
+    _check_tensors(a, b, out, b_layout)
+    dtype = _dtype_code(a)
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    lib = load_library()
+    cfg = _Config()
+    _check(lib.gemm_relu_query_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, b_layout,
+                                      config, splits, ctypes.byref(cfg)))
+    ws_ptr, ws_bytes = None, 0
+    if cfg.workspace_bytes > 0:
+        if workspace is None:
+            workspace = splitk_workspace(a.device, s, cfg.workspace_bytes)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(a.device):
+        rc = lib.gemm_relu_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, b_layout, config,
+                                  splits, ws_ptr, ws_bytes, s.cuda_stream or None)
+    _check(rc)
+    return out
+
+
+def selected_splitk_config(M: int, N: int, K: int, dtype: int = F16, config: int = CONFIG_AUTO, splits: int = 0,
+                           a_ptr: int = 256, b_ptr: int = 256, c_ptr: int = 1 << 40, b_layout: int = B_KN) -> dict:
+    """The configuration gemm_relu_splitk would use, with ``splits`` and ``workspace_bytes`` (host only)."""
+    cfg = _Config()
+    _check(load_library().gemm_relu_query_splitk(a_ptr, b_ptr, c_ptr, M, N, K, dtype, b_layout, config, splits,
+                                                 ctypes.byref(cfg)))
+    return {f: getattr(cfg, f) for f, _ in _Config._fields_}
 
 
 def selected_config(M: int, N: int, K: int, dtype: int = F16, config: int = CONFIG_AUTO,

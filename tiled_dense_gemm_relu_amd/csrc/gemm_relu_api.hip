@@ -12,7 +12,7 @@
 namespace gemm_relu_hip {
 namespace {
 
-constexpr int kVersion = 200;                    // 0.2.0
+constexpr int kVersion = 300;                    // 0.3.0
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 22;
 constexpr int64_t kMaxBand = (int64_t(1) << 31) - 1;   // bytes one buffer descriptor may address
@@ -24,6 +24,8 @@ struct Plan {
     int dma_id;        // DmaId when tile == -4
     int dma_a4, dma_b4;    // 4-byte DMA lanes for A / B (256 LDS-DMA kernel only)
     int b_nk;          // B given as (N, K)
+    int splits;        // K parts per tile (1: no split-K)
+    int64_t counter_bytes;   // split-K workspace: per-tile counters, then the partial tiles
     int vec_pair;      // index into kVecPairs
     int tiles_m, tiles_n;
     int c_vec_ok;
@@ -49,20 +51,36 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes)
 }
 
 // Every check that needs no device.  Fills `plan` on success.
+// Split-K: the LDS-DMA instances that have split-K variants, and the number of
+// work units that split-K aims for (one per CU of an MI355X).
+bool has_splitk(int dma_id) { return dma_id == kDma128 || dma_id == kDma64 || dma_id == kDma64x256; }
+constexpr int kSplitTargetUnits = 256;
+constexpr int kMaxSplits = 64;
+// The workspace starts with a counter region of fixed size, so that partial
+// tiles of one call never land where another call (another shape) keeps its
+// counters: counters, always reset to zero by the call that used them, stay
+// zero from call to call whatever the shapes.
+constexpr int64_t kCounterBytes = 65536;
+
+// splits_req: -1 for the entry points without a workspace (never split), 0 to
+// choose, >= 1 to request that many K parts.
 int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K, int dtype,
-              int b_layout, int config_id, Plan* plan)
+              int b_layout, int config_id, int splits_req, Plan* plan)
 {
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
     if (b_layout != GEMM_RELU_B_KN && b_layout != GEMM_RELU_B_NK) return GEMM_RELU_ERR_BAD_LAYOUT;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
-    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_64)
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_64x256)
         return GEMM_RELU_ERR_BAD_CONFIG;
+    if (splits_req < -1 || splits_req > kMaxSplits) return GEMM_RELU_ERR_INVALID_ARG;
     if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
 
     std::memset(plan, 0, sizeof(*plan));
     plan->cfg.config_id = config_id;
     plan->cfg.b_layout = b_layout;
     plan->b_nk = b_layout == GEMM_RELU_B_NK ? 1 : 0;
+    plan->splits = 1;
+    plan->cfg.splits = 1;
     plan->tile = -3;
     if (M == 0 || N == 0) return GEMM_RELU_OK;        // nothing to compute or write
 
@@ -93,6 +111,10 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     // 4-byte DMA lanes work for rows of an even length with 4-byte aligned bases.
     const bool dword_vectors = va >= 2 && vb >= 2;
     int chosen = config_id;
+    // With split-K on offer, a block of at most 64 rows takes the 64x256 tile:
+    // its K parts restore the parallelism the few tiles lack.
+    if (chosen == GEMM_RELU_CONFIG_AUTO && splits_req >= 0 && full_vectors && M <= 64)
+        chosen = GEMM_RELU_CONFIG_DMA_64x256;
     if (plan->b_nk) {
         // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
         // operands, or 4-byte lanes for both in the 256 one) and the direct
@@ -107,7 +129,8 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         }
         if (chosen == GEMM_RELU_CONFIG_TILE_256) chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_TILE_128) chosen = GEMM_RELU_CONFIG_DMA_128;
-        if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64) && !full_vectors)
+        if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
+             chosen == GEMM_RELU_CONFIG_DMA_64x256) && !full_vectors)
             chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_DIRECT;
     }
@@ -125,7 +148,8 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
             chosen = GEMM_RELU_CONFIG_TILE_128;
     }
     if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
-    if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64) && !full_vectors)
+    if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
+         chosen == GEMM_RELU_CONFIG_DMA_64x256) && !full_vectors)
         chosen = GEMM_RELU_CONFIG_TILE_128;
     plan->cfg.config_id = chosen;
 
@@ -152,6 +176,21 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         plan->cfg.vec_b = plan->dma_b4 ? 2 : 8;
         plan->cfg.grid = tm * tn;
         plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2;
+        if (splits_req >= 0 && has_splitk(id)) {
+            const int64_t tiles = tm * tn, kt = ceil_div(K, g.bk);
+            int64_t s = splits_req;
+            if (s == 0) s = tiles >= 192 ? 1 : ceil_div(kSplitTargetUnits, tiles);
+            s = std::min<int64_t>(s, std::min<int64_t>(kt, kMaxSplits));
+            if (tiles * (g.threads / 64) * 4 > kCounterBytes) s = 1;   // one counter per tile and wave
+            if (s > 1) {
+                if (tiles * s > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
+                plan->splits = (int)s;
+                plan->counter_bytes = kCounterBytes;
+                plan->cfg.splits = (int)s;
+                plan->cfg.grid = tiles * s;
+                plan->cfg.workspace_bytes = plan->counter_bytes + tiles * s * g.bm * g.bn * 4;
+            }
+        }
         return GEMM_RELU_OK;
     }
 
@@ -223,7 +262,7 @@ int check_device(int* cus)
 }
 
 int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
-           int cus, hipStream_t stream)
+           int cus, void* workspace, hipStream_t stream)
 {
     const DtypeKernels& ks = dtype == GEMM_RELU_F16 ? kernels_f16() : kernels_bf16();
     int m = (int)M, n = (int)N, k = (int)K;
@@ -237,20 +276,38 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &c_vec_ok};
         err = hipLaunchKernel(p.b_nk ? ks.direct_nt : ks.direct, dim3((unsigned)p.cfg.grid), dim3(64), args, 0,
                               stream);
-    } else {
+    } else if (p.tile >= 0) {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
-        const int ktail = p.tile == -4 && K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0;
-        const void* fn = p.tile != -4 ? ks.tiled[p.tile][p.vec_pair]
+        err = hipLaunchKernel(ks.tiled[p.tile][p.vec_pair], dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads),
+                              args, 0, stream);
+    } else {
+        int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok, splits = p.splits;
+        int* counters = p.splits > 1 ? static_cast<int*>(workspace) : nullptr;
+        float* ws = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.counter_bytes)
+                                 : nullptr;
+        void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok, &ws, &counters, &splits};
+        const int ktail = K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0;
+        const void* fn = p.splits > 1 ? ks.splitk[p.b_nk][p.dma_id][ktail]
                        : p.b_nk ? (p.dma_id == kDma256 && p.dma_a4 ? ks.dma256_nt_dw[ktail] : ks.dma_nt[p.dma_id][ktail])
                        : p.dma_id == kDma256 ? ks.dma256_dw[p.dma_a4][p.dma_b4][ktail]
                                              : ks.dma[p.dma_id][ktail];
         // The LDS-DMA kernels are persistent: one workgroup per CU (their LDS
-        // ring fills a CU), each walking every grid-th tile.
-        const int64_t grid = p.tile == -4 ? std::min<int64_t>(p.cfg.grid, cus) : p.cfg.grid;
+        // ring fills a CU), each walking every grid-th work unit.
+        const int64_t grid = std::min<int64_t>(p.cfg.grid, cus);
         err = hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     }
     return err == hipSuccess ? GEMM_RELU_OK : GEMM_RELU_ERR_LAUNCH;
+}
+
+int run(const Plan& p, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+        void* workspace, void* stream)
+{
+    if (p.tile == -3) return GEMM_RELU_OK;          // M == 0 or N == 0
+    int cus = 0;
+    const int rc = check_device(&cus);
+    if (rc != GEMM_RELU_OK) return rc;
+    return launch(p, A, B, C, M, N, K, dtype, cus, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -264,7 +321,7 @@ int gemm_relu_query_config_ex(const void* A, const void* B, const void* C, int64
                               int dtype, int b_layout, int config_id, gemm_relu_config_t* out)
 {
     Plan p;
-    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, &p);
+    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, -1, &p);
     if (rc == GEMM_RELU_OK && out) *out = p.cfg;
     return rc;
 }
@@ -279,13 +336,9 @@ int gemm_relu_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, in
                  int config_id, void* stream)
 {
     Plan p;
-    int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, &p);
+    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, -1, &p);
     if (rc != GEMM_RELU_OK) return rc;
-    if (p.tile == -3) return GEMM_RELU_OK;          // M == 0 or N == 0
-    int cus = 0;
-    rc = check_device(&cus);
-    if (rc != GEMM_RELU_OK) return rc;
-    return launch(p, A, B, C, M, N, K, dtype, cus, static_cast<hipStream_t>(stream));
+    return run(p, A, B, C, M, N, K, dtype, nullptr, stream);
 }
 
 int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
@@ -297,6 +350,34 @@ int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int6
 int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype, void* stream)
 {
     return gemm_relu_ex(A, B, C, M, N, K, dtype, GEMM_RELU_B_KN, GEMM_RELU_CONFIG_AUTO, stream);
+}
+
+int gemm_relu_query_splitk(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                           int b_layout, int config_id, int splits, gemm_relu_config_t* out)
+{
+    Plan p;
+    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, splits < 0 ? -2 : splits, &p);
+    if (rc == GEMM_RELU_OK && out) *out = p.cfg;
+    return rc;
+}
+
+int gemm_relu_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                     int b_layout, int config_id, int splits, void* workspace, int64_t workspace_bytes,
+                     void* stream)
+{
+    Plan p;
+    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, splits < 0 ? -2 : splits, &p);
+    if (rc != GEMM_RELU_OK) return rc;
+    if (p.splits > 1) {
+        if (!workspace || workspace_bytes < p.cfg.workspace_bytes ||
+            reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            return GEMM_RELU_ERR_WORKSPACE;
+        const int64_t need = p.cfg.workspace_bytes;
+        if (overlaps(workspace, need, C, 2 * M * N) || overlaps(workspace, need, A, 2 * M * K) ||
+            overlaps(workspace, need, B, 2 * K * N))
+            return GEMM_RELU_ERR_ALIAS;
+    }
+    return run(p, A, B, C, M, N, K, dtype, workspace, stream);
 }
 
 const char* gemm_relu_strerror(int code)
@@ -312,6 +393,7 @@ const char* gemm_relu_strerror(int code)
     case GEMM_RELU_ERR_TOO_LARGE: return "dimensions exceed the supported range";
     case GEMM_RELU_ERR_BAD_CONFIG: return "unknown kernel configuration id";
     case GEMM_RELU_ERR_BAD_LAYOUT: return "unknown B layout (expected GEMM_RELU_B_KN or GEMM_RELU_B_NK)";
+    case GEMM_RELU_ERR_WORKSPACE: return "split-K workspace missing, too small or not 256-byte aligned";
     default: return "unknown error code";
     }
 }

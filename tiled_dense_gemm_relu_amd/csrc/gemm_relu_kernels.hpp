@@ -45,6 +45,7 @@ namespace gemm_relu_hip {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -512,10 +513,19 @@ struct DmaConfig {
 // KTAIL: K is not a multiple of BK, so the last stage is partial and its A
 // pieces past K are masked (K must still be a multiple of the piece: 8
 // elements for 16-byte lanes, 2 for 4-byte lanes).
-template <class Cfg, int DT, bool KTAIL>
+// SPLITK: each tile's K range is cut into `splits` contiguous parts, each a
+// work unit of its own (for shapes with fewer tiles than CUs).  When a unit
+// finishes, each of its waves writes its fp32 partial sub-tile to `ws` and
+// counts itself in `counters[tile * WAVES + wave]`; the wave that finds all
+// other parts counted adds their partials in part order (so the result does
+// not depend on which part finishes last), applies ReLU, stores C and resets
+// the counter to zero.  Nothing ever waits for another wave or workgroup.
+// Without SPLITK, `ws`, `counters` and `splits` are unused.
+template <class Cfg, int DT, bool KTAIL, bool SPLITK = false>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok)
+    int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok,
+    float* __restrict__ ws, int* __restrict__ counters, int splits_arg)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
     constexpr int QA = Cfg::QA, QB = Cfg::QB, NQ = Cfg::NQ, FM = Cfg::FM, FN = Cfg::FN;
@@ -527,17 +537,36 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
-    // Persistent workgroups: workgroup b computes tiles b, b + G, b + 2G, ...
-    // (G = gridDim.x, a multiple of 8 or all tiles), and all K-steps of all its
-    // tiles form one stream through the LDS ring, so the first stages of the
-    // next tile are loaded while the current tile finishes.
-    const int total_tiles = tiles_m * tiles_n;
-    const int n_tiles = (total_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    // Persistent workgroups: workgroup b computes work units b, b + G, b + 2G,
+    // ... (G = gridDim.x, a multiple of 8 or all units), and all K-steps of all
+    // its units form one stream through the LDS ring, so the first stages of
+    // the next unit are loaded while the current one finishes.  A unit is a
+    // tile, or with SPLITK one of its `splits` K ranges (unit u: tile u /
+    // splits, part u % splits, K-steps [part * KT / splits, (part + 1) * KT /
+    // splits)).
+    const int splits = SPLITK ? splits_arg : 1;
+    const int total_units = tiles_m * tiles_n * splits;
+    const int n_units = (total_units - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int KT = (K + BK - 1) / BK;
-    const int steps = n_tiles * KT;
-    auto tile_origin = [&](int i, int& m0, int& n0) {
+    auto unit_info = [&](int i, int& tile, int& part, int& kt0, int& kt1) {
+        const int u = (int)blockIdx.x + i * (int)gridDim.x;
+        tile = u / splits;
+        part = u - tile * splits;
+        kt0 = part * KT / splits;
+        kt1 = (part + 1) * KT / splits;
+    };
+    int steps = n_units * KT;
+    if constexpr (SPLITK) {
+        steps = 0;
+        for (int i = 0; i < n_units; ++i) {
+            int t, pt, k0, k1;
+            unit_info(i, t, pt, k0, k1);
+            steps += k1 - k0;
+        }
+    }
+    auto tile_origin = [&](int tile, int& m0, int& n0) {
         int tm, tn;
-        tile_coords((int)blockIdx.x + i * (int)gridDim.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
+        tile_coords(tile, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
         m0 = tm * BM;
         n0 = tn * BN;
     };
@@ -580,12 +609,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     }
     const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
 
-    // The load side of the stream: the tile and K-step the next DMA belongs to.
-    int f_tile = 0, f_kt = 0, f_m0 = 0, f_n0 = 0;
+    // The load side of the stream: the unit and K-step the next DMA belongs to.
+    int f_unit = 0, f_kt = 0, f_kt_end = 0, f_m0 = 0, f_n0 = 0;
     int32x4_t f_rsrc_a = rsrc_none, f_rsrc_bt = rsrc_none;
     auto fill_tile_setup = [&]() {
-        if (f_tile < n_tiles) {
-            tile_origin(f_tile, f_m0, f_n0);
+        if (f_unit < n_units) {
+            int tile, part;
+            unit_info(f_unit, tile, part, f_kt, f_kt_end);
+            tile_origin(tile, f_m0, f_n0);
             // rows f_m0 .. f_m0 + valid_m - 1 of A; rows past M read as zero
             const int valid_m = min(BM, M - f_m0);
             f_rsrc_a = rsrc_words(A + (size_t)f_m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
@@ -606,7 +637,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // descriptor: nothing is fetched.
     auto dma = [&](int slot, int q) {
         const int k0 = f_kt * BK;
-        const bool live = f_tile < n_tiles;
+        const bool live = f_unit < n_units;
         if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
             if (KTAIL) {   // pieces past K read as zero (K is a multiple of the piece length)
@@ -634,9 +665,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         }
     };
     auto fill_advance = [&]() {
-        if (++f_kt == KT) {
-            f_kt = 0;
-            ++f_tile;
+        if (++f_kt == f_kt_end) {
+            ++f_unit;
             fill_tile_setup();
         }
     };
@@ -698,9 +728,84 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     };
     constexpr int NF = FM + FN, NMF = FM * FN;
 
-    // The compute side of the stream: the tile being accumulated.
-    int c_tile = 0, c_kt = 0, c_m0, c_n0;
-    tile_origin(0, c_m0, c_n0);
+    // The compute side of the stream: the unit being accumulated.
+    int c_unit = 0, c_tile, c_part, c_kt, c_kt_end, c_m0, c_n0;
+    unit_info(0, c_tile, c_part, c_kt, c_kt_end);
+    tile_origin(c_tile, c_m0, c_n0);
+
+    // SPLITK: combine the parts of tile c_tile, wave by wave: wave w of every
+    // part owns the same sub-tile, and counts itself in counters[tile * WAVES
+    // + w].  The wave that finds the other parts counted holds the last part:
+    // it adds theirs and returns true (it stores that sub-tile).  Waves never
+    // wait for each other or for other workgroups.
+    //  The parts of a tile run on different XCDs, whose L2s are not coherent
+    //  with each other.  Partials are therefore written and read with
+    //  device-scope (sc1) buffer accesses, coherent without any L2 write-back
+    //  or invalidate, and a wave's partial stores have completed (vmcnt 0)
+    //  before it counts itself.
+    //  Partial layout: tile t, part p, wave w, block (i, j), quarter q, lane l:
+    //  4 floats at ((((t * splits + p) * WAVES + w) * FN + i) * FM + j) * 1024
+    //  + q * 256 + l * 4, so each quarter of a block is one contiguous 1 KiB.
+    auto combine_parts = [&](floatx16 (&sum)[FN][FM]) -> bool {
+        constexpr int BLOCK_BYTES = 4096;
+        constexpr int kDeviceScope = 16;   // cache policy sc1: coherent at device scope
+        const uint32_t tile_bytes = (uint32_t)Cfg::BM * (uint32_t)Cfg::BN * 4u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(ws + (size_t)c_tile * (size_t)splits * (tile_bytes / 4),
+                                                    (uint32_t)splits * tile_bytes);
+        auto part_off = [&](int part, int i, int j) {
+            return (uint32_t)part * tile_bytes + (uint32_t)((wave * FN + i) * FM + j) * BLOCK_BYTES + lane * 16;
+        };
+        int* const cnt = counters + (size_t)c_tile * Cfg::WAVES + wave;
+        // If every other part has already counted itself, this one is last
+        // and need not publish its own partial.
+        int seen = 0;
+        if (lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool last = __builtin_amdgcn_readfirstlane(seen) == splits - 1;
+        if (!last) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const floatx4 v = {sum[i][j][4 * q], sum[i][j][4 * q + 1], sum[i][j][4 * q + 2],
+                                           sum[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                                               part_off(c_part, i, j) + q * 1024, 0, kDeviceScope);
+                    }
+            wait_vmcnt<0>();   // the partial has reached device scope before the count
+            int before = 0;
+            if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = __builtin_amdgcn_readfirstlane(before) == splits - 1;
+        }
+        if (!last) return false;
+        asm volatile("" ::: "memory");   // the partial loads stay after the count that allowed them
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                floatx16 total = floatx16{0};
+                for (int part = 0; part < splits; ++part) {
+                    if (part == c_part) {
+                        total += sum[i][j];
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const floatx4 v = __builtin_bit_cast(
+                                floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, part_off(part, i, j) + q * 1024, 0,
+                                                                              kDeviceScope));
+                            total[4 * q] += v[0];
+                            total[4 * q + 1] += v[1];
+                            total[4 * q + 2] += v[2];
+                            total[4 * q + 3] += v[3];
+                        }
+                    }
+                }
+                sum[i][j] = total;
+            }
+        if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    };
 
     // Prologue: steps 0 .. S-2 in flight, step 0 landed, its first k-step read.
 #pragma unroll
@@ -752,19 +857,30 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             }
             if (ks == 0) fill_advance();
         }
-        if (++c_kt == KT) {
-            // Fused epilogue of the finished tile: ReLU, round to the dtype,
-            // masked store; then start the next tile from zero.
+        if (++c_kt == c_kt_end) {
+            // Fused epilogue of the finished unit: ReLU, round to the dtype,
+            // masked store (with SPLITK, by the last part of the tile, after
+            // the partial sums are combined); then start the next unit from zero.
+            bool store = true;
+            if constexpr (SPLITK) {
+                if (splits > 1) store = combine_parts(acc);
+            }
+            if (store) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        store_block<DT>(C, acc[i][j], lane, c_m0 + wm * WTM + j * 32, c_n0 + wn * WTN + i * 32, M,
+                                        N, c_vec_ok != 0);
+            }
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    store_block<DT>(C, acc[i][j], lane, c_m0 + wm * WTM + j * 32, c_n0 + wn * WTN + i * 32, M, N,
-                                    c_vec_ok != 0);
-                    acc[i][j] = floatx16{0};
-                }
-            c_kt = 0;
-            if (++c_tile < n_tiles) tile_origin(c_tile, c_m0, c_n0);
+                for (int j = 0; j < FM; ++j) acc[i][j] = floatx16{0};
+            if (++c_unit < n_units) {
+                unit_info(c_unit, c_tile, c_part, c_kt, c_kt_end);
+                tile_origin(c_tile, c_m0, c_n0);
+            }
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -778,11 +894,14 @@ using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;   // ... with B
 using DmaTile256AB4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4>;   // ... both
 using DmaTile128 = DmaConfig<128, 128, 64, 4, 2, 2, 4>;   // mid shapes: 4 waves of 64x64
 using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny shapes: 4 waves of 32x32, 8 stages
+// few rows, many columns (with split-K): 4 waves of 64x64, 8 stages, 7 x 16 KiB of B in flight
+using DmaTile64x256 = DmaConfig<64, 256, 32, 8, 1, 4, 4>;
 // B given as B^T, (N, K) row-major
 using DmaTile256T = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 16, true>;
 using DmaTile256T4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4, true>;    // K even but not a multiple of 8
 using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
 using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
+using DmaTile64x256T = DmaConfig<64, 256, 32, 8, 1, 4, 4, 16, 16, true>;
 
 // ---------------------------------------------------------------- direct kernel
 

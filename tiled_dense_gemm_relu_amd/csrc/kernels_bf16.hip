@@ -21,7 +21,8 @@ constexpr bool dma_geom_matches = Cfg::BM == kDmaGeom[id].bm && Cfg::BN == kDmaG
 static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
                   dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
                   dma_geom_matches<DmaTile256T4, kDma256> && dma_geom_matches<DmaTile128T, kDma128> &&
-                  dma_geom_matches<DmaTile64T, kDma64>,
+                  dma_geom_matches<DmaTile64T, kDma64> && dma_geom_matches<DmaTile64x256, kDma64x256> &&
+                  dma_geom_matches<DmaTile64x256T, kDma64x256>,
               "host DMA tile geometry out of date");
 
 template <class Cfg>
@@ -35,9 +36,18 @@ void fill_row(const void** row)
     row[5] = (const void*)&gemm_relu_tiled<Cfg, kBF16, 1, 1>;
 }
 
+template <class KN, class NK>
+void fill_splitk(DtypeKernels& t, int id)
+{
+    t.splitk[0][id][0] = (const void*)&gemm_relu_dma<KN, kBF16, false, true>;
+    t.splitk[0][id][1] = (const void*)&gemm_relu_dma<KN, kBF16, true, true>;
+    t.splitk[1][id][0] = (const void*)&gemm_relu_dma<NK, kBF16, false, true>;
+    t.splitk[1][id][1] = (const void*)&gemm_relu_dma<NK, kBF16, true, true>;
+}
+
 DtypeKernels make_table()
 {
-    DtypeKernels t;
+    DtypeKernels t{};
     fill_row<Tile256>(t.tiled[kTile256]);
     fill_row<Tile128>(t.tiled[kTile128]);
     t.direct = (const void*)&gemm_relu_direct<kBF16>;
@@ -64,6 +74,13 @@ DtypeKernels make_table()
     t.dma_nt[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64T, kBF16, true>;
     t.dma256_nt_dw[0] = (const void*)&gemm_relu_dma<DmaTile256T4, kBF16, false>;
     t.dma256_nt_dw[1] = (const void*)&gemm_relu_dma<DmaTile256T4, kBF16, true>;
+    t.dma[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256, kBF16, false>;
+    t.dma[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256, kBF16, true>;
+    t.dma_nt[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256T, kBF16, false>;
+    t.dma_nt[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256T, kBF16, true>;
+    fill_splitk<DmaTile128, DmaTile128T>(t, kDma128);
+    fill_splitk<DmaTile64, DmaTile64T>(t, kDma64);
+    fill_splitk<DmaTile64x256, DmaTile64x256T>(t, kDma64x256);
     return t;
 }
 }  // namespace

@@ -50,9 +50,10 @@ class Workload:
         return 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
 
 
-# The five workload shapes: a small correctness case, the 1024^3 example shape
-# with 128x128x64 tiles, the 8192^3 compute-bound headline, a shape with ragged
-# M, N and K tails, and a skinny decode-like bf16 shape that is HBM-bound.
+# The workload shapes: a small correctness case, the 1024^3 example shape with
+# 128x128x64 tiles, the 8192^3 compute-bound headline, a shape with ragged M, N
+# and K tails, a skinny decode-like bf16 shape that is HBM-bound, and a deep-K
+# shape with few output tiles.
 WORKLOADS = {
     "small_256": Workload("small_256", 256, 256, 256, "fp16", 1.0, 1001, 1011),
     "square_1024": Workload("square_1024", 1024, 1024, 1024, "fp16", 1.0, 1002, 1012),
@@ -61,6 +62,8 @@ WORKLOADS = {
                                        1004, 1014),
     "skinny_64x16384x8192": Workload("skinny_64x16384x8192", 64, 16384, 8192, "bf16", 0.05,
                                      1005, 1015),
+    # few output tiles over a long K: the case split-K is for
+    "deep_512x512x16384": Workload("deep_512x512x16384", 512, 512, 16384, "fp16", 0.05, 1006, 1016),
 }
 
 
