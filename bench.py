@@ -209,7 +209,7 @@ def main():
                 ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, 4),
                 ("ragged_4000x11000x4100", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, None),
-                ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, 0),
+                ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_DMA_64x256, 4),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
                 ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None)]

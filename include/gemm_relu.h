@@ -82,7 +82,11 @@ enum {
 };
 
 /* Kernel configuration ids for gemm_relu_with_config (GEMM_RELU_CONFIG_AUTO
- * lets the library choose, as gemm_relu does). */
+ * lets the library choose, as gemm_relu does).  AUTO first looks the exact
+ * shape (M, N, K, dtype, B layout) up in a table of shapes measured on an
+ * MI355X by tiled_dense_gemm_relu_amd/tune.py (compiled in from
+ * csrc/tuned_table.inc; it applies when A and B are aligned for the widest
+ * loads their row lengths allow, as in the tuner), else it uses size rules. */
 enum {
     GEMM_RELU_CONFIG_AUTO = -1,
     GEMM_RELU_CONFIG_DIRECT = 0,      /* one wave per 32x32 block, operands from global memory */

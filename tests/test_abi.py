@@ -185,8 +185,10 @@ def test_b_nk_forced_configs():
 
 
 def test_splitk_config_choice():
-    skinny = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16)
+    # an untuned skinny shape: the 64x256 tile with enough parts for 256 units
+    skinny = gr.selected_splitk_config(64, 16384, 8192 + 64, dtype=gr.BF16)
     assert (skinny["config_id"], skinny["splits"], skinny["grid"]) == (6, 4, 256)
+    skinny = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16, config=6)
     # the fixed 64 KiB counter region + 4 fp32 partial tiles per tile
     assert skinny["workspace_bytes"] == 65536 + 64 * 4 * 64 * 256 * 4
     # enough tiles already: no split, no workspace
@@ -218,3 +220,35 @@ def test_splitk_argument_errors(lib):
     assert lib.gemm_relu_splitk(*args, 4, ws + 16, need, None) == -10             # misaligned
     assert lib.gemm_relu_splitk(*args, 4, C_PTR, need, None) == -3                # overlaps C
     assert lib.gemm_relu_splitk(A_PTR, B_PTR, C_PTR, 64, 512, 512, 0, 2, -1, 4, ws, need, None) == -9
+
+
+def tuned_table():
+    """Rows of the compiled-in table, parsed from its source."""
+    path = os.path.join(ROOT, "tiled_dense_gemm_relu_amd", "csrc", "tuned_table.inc")
+    rows = []
+    for line in open(path):
+        m = re.match(r"\{(.*)\},\s*$", line.strip())
+        if m:
+            rows.append(tuple(int(v) for v in m.group(1).split(",")))
+    return rows
+
+
+def test_tuned_table_rows_are_what_auto_selects():
+    rows = tuned_table()
+    assert len(rows) >= 10
+    assert len({r[:5] for r in rows}) == len(rows)                       # one row per shape
+    for M, N, K, dt, layout, config, sk_config, splits in rows:
+        assert 0 <= config <= 6 and 0 <= sk_config <= 6 and 1 <= splits <= 64
+        plain = gr.selected_config(M, N, K, dtype=dt, b_layout=layout)
+        assert (plain["config_id"], plain["splits"]) == (config, 1), (M, N, K, layout)
+        sk = gr.selected_splitk_config(M, N, K, dtype=dt, b_layout=layout)
+        assert (sk["config_id"], sk["splits"]) == (sk_config, splits), (M, N, K, layout)
+
+
+def test_tuned_table_needs_the_tuners_alignment():
+    # The deep shape is tuned to split in 4; with B only 4-byte aligned the
+    # table does not apply and the heuristics choose (the register-staged 128 tile).
+    rows = {r[:5]: r for r in tuned_table()}
+    assert rows[(512, 512, 16384, 0, 0)][5:] == (5, 5, 4)
+    sk = gr.selected_splitk_config(512, 512, 16384, b_ptr=(1 << 20) + 4)
+    assert (sk["config_id"], sk["splits"]) == (2, 1)

@@ -96,10 +96,11 @@ def test_splitk_matches_integer_results_of_the_plain_kernel():
 @pytest.mark.parametrize("b_layout", [gr.B_KN, gr.B_NK])
 def test_splitk_skinny_64x16384x8192_bf16_full(integer, b_layout):
     w = inputs.WORKLOADS["skinny_64x16384x8192"]
-    cfg = gr.selected_splitk_config(w.M, w.N, w.K, dtype=gr.BF16, b_layout=b_layout)
+    cfg = gr.selected_splitk_config(w.M, w.N, w.K, dtype=gr.BF16, config=binding.CONFIG_DMA_64x256,
+                                    b_layout=b_layout)
     assert (cfg["config_id"], cfg["splits"]) == (binding.CONFIG_DMA_64x256, 4)
     a, b = inputs.workload_inputs(w, integer)
-    got = run_splitk(a, b, b_layout, binding.CONFIG_AUTO, 0)
+    got = run_splitk(a, b, b_layout, binding.CONFIG_DMA_64x256, 0)
     say(f"[{w.name} split-K layout={b_layout} integer={integer}] full oracle")
     want = oracle.gemm_relu(a, b, w.dtype)
     check_relu_invariants(got, w.dtype)

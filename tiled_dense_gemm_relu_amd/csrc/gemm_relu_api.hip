@@ -62,6 +62,33 @@ constexpr int kMaxSplits = 64;
 // zero from call to call whatever the shapes.
 constexpr int64_t kCounterBytes = 65536;
 
+// Shapes measured by tune.py on an MI355X: the fastest configuration of the
+// plain entry points and of the split-K one.  The last row is a sentinel (M == 0
+// never reaches the lookup).
+struct TunedShape {
+    int64_t m, n, k;
+    int dtype, b_layout, config, splitk_config, splits;
+};
+constexpr TunedShape kTuned[] = {
+#include "tuned_table.inc"
+    {0, 0, 0, 0, 0, 0, 0, 0},
+};
+
+const TunedShape* find_tuned(int64_t M, int64_t N, int64_t K, int dtype, int b_layout)
+{
+    for (const TunedShape& t : kTuned)
+        if (t.m == M && t.n == N && t.k == K && t.dtype == dtype && t.b_layout == b_layout) return &t;
+    return nullptr;
+}
+
+// Widest load the row length allows (the width of aligned pointers).
+int row_width(int64_t row_len)
+{
+    for (int v = 8; v > 1; v /= 2)
+        if (row_len % v == 0) return v;
+    return 1;
+}
+
 // splits_req: -1 for the entry points without a workspace (never split), 0 to
 // choose, >= 1 to request that many K parts.
 int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K, int dtype,
@@ -111,6 +138,13 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     // 4-byte DMA lanes work for rows of an even length with 4-byte aligned bases.
     const bool dword_vectors = va >= 2 && vb >= 2;
     int chosen = config_id;
+    // A tuned shape, with pointers aligned as the tuner's were: its measured best.
+    if (chosen == GEMM_RELU_CONFIG_AUTO && va == row_width(K) && vb == row_width(plan->b_nk ? K : N)) {
+        if (const TunedShape* t = find_tuned(M, N, K, dtype, b_layout)) {
+            chosen = splits_req >= 0 ? t->splitk_config : t->config;
+            if (splits_req == 0) splits_req = t->splits;
+        }
+    }
     // With split-K on offer, a block of at most 64 rows takes the 64x256 tile:
     // its K parts restore the parallelism the few tiles lack.
     if (chosen == GEMM_RELU_CONFIG_AUTO && splits_req >= 0 && full_vectors && M <= 64)
