@@ -212,10 +212,11 @@ def main():
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_DMA_64x256, 4),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
-                ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None)]
+                ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None),
+                ("square_8192", binding.B_KN, binding.CONFIG_DMA_256x128_WS, None)]
         for name, b_layout, s_config, s_splits in runs:
             sw = inputs.WORKLOADS[name]
-            if (sw.name == w.name and s_splits is None and
+            if (sw.name == w.name and s_splits is None and s_config == binding.CONFIG_AUTO and
                     args.b_layout == ("nk" if b_layout == binding.B_NK else "kn")):
                 continue
             s_ms, s_kms = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, config=s_config,
@@ -224,6 +225,8 @@ def main():
                 name += "_b_nk"
             if s_splits is not None:
                 name += "_splitk" if s_config == binding.CONFIG_AUTO else f"_splitk{s_splits}_config{s_config}"
+            elif s_config != binding.CONFIG_AUTO:
+                name += "_" + binding.CONFIG_NAMES[s_config]
             entry = {"ms": round(s_kms, 5), "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
                      "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}

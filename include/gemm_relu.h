@@ -97,12 +97,14 @@ enum {
     GEMM_RELU_CONFIG_DMA_128 = 4,     /* 128x128x64 block tile, 4 waves, 4 direct-to-LDS stages */
     GEMM_RELU_CONFIG_DMA_64 = 5,      /* 64x64x64 block tile, 4 waves, 8 direct-to-LDS stages
                                          (small, skinny and bandwidth-bound shapes) */
-    GEMM_RELU_CONFIG_DMA_64x256 = 6   /* 64x256x32 block tile, 4 waves, 8 direct-to-LDS stages
+    GEMM_RELU_CONFIG_DMA_64x256 = 6,  /* 64x256x32 block tile, 4 waves, 8 direct-to-LDS stages
                                          (few rows, many columns; meant for split-K) */
-    /* DMA_128, DMA_64 and DMA_64x256 need 16-byte loads of A and B (K % 8 == 0, N % 8 == 0,
-       16-byte aligned A and B); DMA_256 also takes 4-byte loads (K and N even, 4-byte aligned
-       A and B).  For other inputs a DMA_* request falls back to TILE_256 (DMA_256) or TILE_128
-       (DMA_128, DMA_64, DMA_64x256). */
+    GEMM_RELU_CONFIG_DMA_256x128_WS = 7 /* 256x128x32 block tile, 4 direct-to-LDS stages, wave-
+                                         specialised: 8 compute waves and 4 waves that only load */
+    /* DMA_128, DMA_64, DMA_64x256 and DMA_256x128_WS need 16-byte loads of A and B (K % 8 == 0,
+       N % 8 == 0, 16-byte aligned A and B); DMA_256 also takes 4-byte loads (K and N even,
+       4-byte aligned A and B).  For other inputs a DMA_* request falls back to TILE_256
+       (DMA_256, DMA_256x128_WS) or TILE_128 (DMA_128, DMA_64, DMA_64x256). */
 };
 
 /* What a configuration is, for reports and tests. */

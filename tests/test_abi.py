@@ -85,7 +85,7 @@ def test_unknown_b_layout_is_rejected(lib):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 7, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 8, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -252,3 +252,15 @@ def test_tuned_table_needs_the_tuners_alignment():
     assert rows[(512, 512, 16384, 0, 0)][5:] == (5, 5, 4)
     sk = gr.selected_splitk_config(512, 512, 16384, b_ptr=(1 << 20) + 4)
     assert (sk["config_id"], sk["splits"]) == (2, 1)
+
+
+def test_wave_specialised_config():
+    cfg = gr.selected_config(8192, 8192, 8192, config=7)
+    assert (cfg["config_id"], cfg["block_m"], cfg["block_n"], cfg["block_k"], cfg["threads"]) == (7, 256, 128, 32, 768)
+    assert (cfg["grid"], cfg["lds_bytes"]) == (32 * 64, 4 * 384 * 32 * 2)
+    assert gr.selected_config(8192, 8192, 8192, config=7, b_layout=gr.B_NK)["config_id"] == 7
+    # needs 16-byte loads: else the 256 tile of the layout's fallback family
+    assert gr.selected_config(512, 512, 516, config=7)["config_id"] == 1
+    assert gr.selected_config(512, 512, 516, config=7, b_layout=gr.B_NK)["config_id"] == 3
+    # never split
+    assert gr.selected_splitk_config(512, 512, 4096, config=7, splits=4)["splits"] == 1

@@ -476,10 +476,14 @@ __device__ __forceinline__ int b_swizzle(int k)
 }
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_,
-          int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16, bool B_KMAJOR_ = false>
+          int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16, bool B_KMAJOR_ = false, int PRODUCERS_ = 0>
 struct DmaConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, GROUP_M = GROUP_M_;
-    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+    // WAVES compute waves; PRODUCERS > 0 adds that many waves that only issue
+    // the LDS DMA (wave specialisation), else every compute wave loads its share.
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N;
+    static constexpr int PRODUCERS = PRODUCERS_, DMA_WAVES = PRODUCERS > 0 ? PRODUCERS : WAVES;
+    static constexpr int THREADS = 64 * (WAVES + PRODUCERS);
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;     // wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;               // 32x32 MFMA blocks per wave
     static constexpr int NKS = BK / 16;                              // MFMA k-steps per stage
@@ -494,14 +498,14 @@ struct DmaConfig {
     // rows of a multiple of 8 elements) or 4 (buffer_load_dword, rows of an even
     // number of elements).
     static constexpr int A_LANE_BYTES = A_LANE_BYTES_, B_LANE_BYTES = B_LANE_BYTES_;
-    static constexpr int QA = A_STAGE / (64 * A_LANE_BYTES) / WAVES; // DMA instructions per wave per stage
-    static constexpr int QB = B_STAGE / (64 * B_LANE_BYTES) / WAVES;
+    static constexpr int QA = A_STAGE / (64 * A_LANE_BYTES) / DMA_WAVES; // DMA instructions per wave per stage
+    static constexpr int QB = B_STAGE / (64 * B_LANE_BYTES) / DMA_WAVES;
     static constexpr int NQ = QA + QB;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of whole 32x32 MFMA blocks");
     static_assert(BK % 32 == 0, "an even number of 16-deep MFMA k-steps per stage");
     static_assert((A_LANE_BYTES == 16 || A_LANE_BYTES == 4) && (B_LANE_BYTES == 16 || B_LANE_BYTES == 4),
                   "dwordx4 or dword DMA");
-    static_assert(QA * WAVES * 64 * A_LANE_BYTES == A_STAGE && QB * WAVES * 64 * B_LANE_BYTES == B_STAGE,
+    static_assert(QA * DMA_WAVES * 64 * A_LANE_BYTES == A_STAGE && QB * DMA_WAVES * 64 * B_LANE_BYTES == B_STAGE,
                   "stages split evenly into DMA instructions");
     static_assert((STAGES & (STAGES - 1)) == 0 && STAGES >= 2, "power-of-two ring of at least 2 stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
@@ -536,6 +540,11 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+    // With producer waves, waves WAVES .. WAVES + PRODUCERS - 1 issue every DMA
+    // and compute nothing; dwave is a wave's index among the loading waves.
+    constexpr bool WS = Cfg::PRODUCERS > 0;
+    const bool producer = WS && wave >= Cfg::WAVES;
+    const int dwave = WS ? wave - Cfg::WAVES : wave;
 
     // Persistent workgroups: workgroup b computes work units b, b + G, b + 2G,
     // ... (G = gridDim.x, a multiple of 8 or all units), and all K-steps of all
@@ -584,7 +593,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     int a_kcol[QA], b_ncol[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-        const int byte = ((wave * QA + q) * 64 + lane) * LA;       // offset inside the A stage
+        const int byte = ((dwave * QA + q) * 64 + lane) * LA;      // offset inside the A stage
         const int row = byte / A_ROW;
         const int lc = ((byte % A_ROW) / 16) ^ a_swizzle<A_ROW>(row);
         const int kcol = lc * 8 + (byte % 16) / 2;                  // first k of this lane's piece
@@ -593,7 +602,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-        const int byte = ((wave * QB + q) * 64 + lane) * LB;       // offset inside the B stage
+        const int byte = ((dwave * QB + q) * 64 + lane) * LB;      // offset inside the B stage
         const int row = byte / B_ROW;
         if constexpr (Cfg::B_KMAJOR) {                              // row = n, K-contiguous like A
             const int lc = ((byte % B_ROW) / 16) ^ a_swizzle<B_ROW>(row);
@@ -644,7 +653,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                 vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
                 so = 0u;
             }
-            dma_issue(live ? f_rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (wave * QA + q) * 64 * LA, vo,
+            dma_issue(live ? f_rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (dwave * QA + q) * 64 * LA, vo,
                       live ? so : 0u, LA);
         } else if constexpr (Cfg::B_KMAJOR) {
             const int qb = q - QA;
@@ -653,14 +662,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                 vo = k0 + b_ncol[qb] < K ? b_voff[qb] + so : kOobOffset;
                 so = 0u;
             }
-            dma_issue(live ? f_rsrc_bt : rsrc_none, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + qb) * 64 * LB,
+            dma_issue(live ? f_rsrc_bt : rsrc_none, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (dwave * QB + qb) * 64 * LB,
                       vo, live ? so : 0u, LB);
         } else {
             // descriptor based at (row k0, column f_n0): rows past K read as zero
             const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
             const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N + f_n0, nb) : rsrc_none;
             const uint32_t vo = f_n0 + b_ncol[q - QA] < N ? b_voff[q - QA] : kOobOffset;   // columns past N
-            dma_issue(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (wave * QB + (q - QA)) * 64 * LB, vo, 0u,
+            dma_issue(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (dwave * QB + (q - QA)) * 64 * LB, vo, 0u,
                       LB);
         }
     };
@@ -808,16 +817,37 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     };
 
     // Prologue: steps 0 .. S-2 in flight, step 0 landed, its first k-step read.
+    if (!WS || producer) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) {
+        for (int s = 0; s < S - 1; ++s) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) dma(s, q);
-        fill_advance();
+            for (int q = 0; q < NQ; ++q) dma(s, q);
+            fill_advance();
+        }
+        wait_vmcnt<(S - 2) * NQ>();
     }
-    wait_vmcnt<(S - 2) * NQ>();
     lds_barrier();
+    if constexpr (WS) {
+        if (producer) {
+            // The producer side of the ring: in step g, refill the slot step
+            // g-1 used (free since the last barrier) with step g+S-1, wait for
+            // step g+1 to land, and meet the compute waves at the barrier they
+            // pass before reading step g+1.  Same barrier count as theirs.
+            for (int g = 0; g < steps; ++g) {
+                const int slot_fill = (g + S - 1) & (S - 1);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) dma(slot_fill, q);
+                fill_advance();
+                wait_vmcnt<(S - 2) * NQ>();
+                lds_barrier();
+            }
+            wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
+            return;
+        }
+    }
 #pragma unroll
     for (int u = 0; u < NF; ++u) read_unit(0, 0, 0, u);
+    constexpr int NQC = WS ? 0 : NQ;   // DMAs a compute wave issues per step
 
     for (int g = 0; g < steps; ++g) {
         const int slot = g & (S - 1);
@@ -829,7 +859,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             const bool last = ks == NKS - 1;
             if (last) {
                 __builtin_amdgcn_s_setprio(0);
-                wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
+                if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
                 lds_barrier();                // ... and for every wave
             }
             // Issue priority 1 for the first k-steps of each K-step (MFMAs and
@@ -840,7 +870,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             // Work spread over this k-step's MFMAs: the next k-step's fragment
             // reads (from the next stage after the barrier), then, in the first
             // k-step, the DMAs of step g+S-1.
-            const int n_items = NF + (ks == 0 ? NQ : 0);
+            const int n_items = NF + (ks == 0 ? NQC : 0);
 #pragma unroll
             for (int t = 0; t < NMF; ++t) {
                 acc[t / FM][t % FM] = mfma_32x32x16<DT>(fa[cur][t / FM], fb[cur][t % FM], acc[t / FM][t % FM]);
@@ -855,7 +885,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (ks == 0) fill_advance();
+            if (!WS && ks == 0) fill_advance();
         }
         if (++c_kt == c_kt_end) {
             // Fused epilogue of the finished unit: ReLU, round to the dtype,
@@ -902,6 +932,11 @@ using DmaTile256T4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4, true>;    // K ev
 using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
 using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
 using DmaTile64x256T = DmaConfig<64, 256, 32, 8, 1, 4, 4, 16, 16, true>;
+// Wave-specialised: 8 compute waves of 64x64 and 4 DMA-only producer waves
+// (12 waves, 3 per SIMD: the 256x256 tile's accumulators leave no room for a
+// producer wave beside its compute waves).
+using DmaTile256x128W = DmaConfig<256, 128, 32, 4, 4, 2, 4, 16, 16, false, 4>;
+using DmaTile256x128WT = DmaConfig<256, 128, 32, 4, 4, 2, 4, 16, 16, true, 4>;
 
 // ---------------------------------------------------------------- direct kernel
 

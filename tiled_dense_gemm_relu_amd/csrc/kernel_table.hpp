@@ -24,7 +24,7 @@ constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 
 struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
     const void* direct;
-    const void* dma[4][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
+    const void* dma[5][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
     // The 256 LDS-DMA kernel with 4-byte DMA lanes: [A 4-byte][B 4-byte][K % BK != 0]
     // (index [0][0] unused: that is dma[kDma256]); need 2-element loads.
     const void* dma256_dw[2][2][2];
@@ -32,21 +32,23 @@ struct DtypeKernels {
     // LDS-DMA kernels with 16-byte lanes by DmaId and [K % BK != 0], and the
     // 256 one with 4-byte lanes by [K % BK != 0].
     const void* direct_nt;
-    const void* dma_nt[4][2];
+    const void* dma_nt[5][2];
     const void* dma256_nt_dw[2];
     // Split-K instances (8-element loads): [B layout][DmaId][K % BK != 0];
-    // null for the 256 tile, which has none.
-    const void* splitk[2][4][2];
+    // null for the 256 tiles, which have none.
+    const void* splitk[2][5][2];
 };
 
 // LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.
-enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kNumDma = 4 };
-// Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64 / DmaTile64x256).
+enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kNumDma = 5 };
+// Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64 / DmaTile64x256 /
+// DmaTile256x128W; threads include the producer waves).
 constexpr TileGeom kDmaGeom[kNumDma] = {
     {256, 256, 32, 4, 512, 4},
     {128, 128, 64, 4, 256, 4},
     {64, 64, 64, 8, 256, 4},
     {64, 256, 32, 8, 256, 4},
+    {256, 128, 32, 4, 768, 4},
 };
 
 const DtypeKernels& kernels_f16();

@@ -22,7 +22,8 @@ static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile1
                   dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
                   dma_geom_matches<DmaTile256T4, kDma256> && dma_geom_matches<DmaTile128T, kDma128> &&
                   dma_geom_matches<DmaTile64T, kDma64> && dma_geom_matches<DmaTile64x256, kDma64x256> &&
-                  dma_geom_matches<DmaTile64x256T, kDma64x256>,
+                  dma_geom_matches<DmaTile64x256T, kDma64x256> && dma_geom_matches<DmaTile256x128W, kDma256x128W> &&
+                  dma_geom_matches<DmaTile256x128WT, kDma256x128W>,
               "host DMA tile geometry out of date");
 
 template <class Cfg>
@@ -78,6 +79,10 @@ DtypeKernels make_table()
     t.dma[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256, kBF16, true>;
     t.dma_nt[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256T, kBF16, false>;
     t.dma_nt[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256T, kBF16, true>;
+    t.dma[kDma256x128W][0] = (const void*)&gemm_relu_dma<DmaTile256x128W, kBF16, false>;
+    t.dma[kDma256x128W][1] = (const void*)&gemm_relu_dma<DmaTile256x128W, kBF16, true>;
+    t.dma_nt[kDma256x128W][0] = (const void*)&gemm_relu_dma<DmaTile256x128WT, kBF16, false>;
+    t.dma_nt[kDma256x128W][1] = (const void*)&gemm_relu_dma<DmaTile256x128WT, kBF16, true>;
     fill_splitk<DmaTile128, DmaTile128T>(t, kDma128);
     fill_splitk<DmaTile64, DmaTile64T>(t, kDma64);
     fill_splitk<DmaTile64x256, DmaTile64x256T>(t, kDma64x256);
