@@ -16,7 +16,10 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 import torch
@@ -69,10 +72,48 @@ def make_sets(w, n_sets, device, b_layout=binding.B_KN):
     return sets
 
 
+def sample_clocks(launch, seconds):
+    """Keep the GPU busy with `launch` for about `seconds` while rocm-smi samples the shader
+    clock (and the package power where the board reports it).  Returns medians over the
+    samples after the first, or None if rocm-smi is unavailable."""
+    samples, stop = [], threading.Event()
+
+    def smi():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--showpower"], capture_output=True,
+                                     text=True, timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            clk = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
+            pwr = re.search(r"(?<!Max )Graphics Package Power \(W\): ([0-9.]+)", out)
+            samples.append((int(clk.group(1)) if clk else None, float(pwr.group(1)) if pwr else None))
+
+    th = threading.Thread(target=smi, daemon=True)
+    th.start()
+    t0, i = time.time(), 0
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    clks = sorted(c for c, _ in samples[1:] if c is not None)
+    pwrs = sorted(p for _, p in samples[1:] if p is not None)
+    if not clks:
+        return None
+    return {"sclk_mhz_median": clks[len(clks) // 2], "sclk_mhz_min": clks[0], "sclk_mhz_max": clks[-1],
+            "power_w_median": pwrs[len(pwrs) // 2] if pwrs else None, "samples": len(clks),
+            "seconds": round(time.time() - t0, 2), "source": "rocm-smi --showclocks --showpower"}
+
+
 def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN,
-                  splits=None):
-    """Returns (ms per step over the timed region, mean kernel ms from per-launch events).
-    splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with that many parts."""
+                  splits=None, clock_seconds=0.0):
+    """Returns (ms per step over the timed region, mean kernel ms from per-launch events, clock
+    samples or None).  splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with
+    that many parts.  clock_seconds > 0: after the timed region, keep launching for that long while
+    rocm-smi samples the clock (outside the timed region)."""
     sets = make_sets(w, n_sets, device, b_layout)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
@@ -116,8 +157,9 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     torch.cuda.synchronize(device)
     total_ms = t0.elapsed_time(t1)
     kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    clocks = sample_clocks(launch, clock_seconds) if clock_seconds > 0 else None
     del sets
-    return total_ms / steps, kernel_ms
+    return total_ms / steps, kernel_ms, clocks
 
 
 def cpu_baseline(w, target_s):
@@ -173,6 +215,9 @@ def main():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
+    p.add_argument("--clock-seconds", type=float, default=2.0,
+                   help="after the timed steps, sustain the workload this long while rocm-smi samples the "
+                        "shader clock (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = p.parse_args()
@@ -196,7 +241,9 @@ def main():
     cfg = gr.selected_config(w.M, w.N, w.K, binding.F16 if w.dtype == "fp16" else binding.BF16, args.config,
                              b_layout=b_layout)
     log(f"[bench] {w.name}: config {cfg}")
-    ms_step, kernel_ms = time_workload(w, args.steps, args.warmup, args.sets, device, args.config, b_layout)
+    ms_step, kernel_ms, clocks = time_workload(w, args.steps, args.warmup, args.sets, device, args.config,
+                                               b_layout, clock_seconds=args.clock_seconds)
+    log(f"[bench] clocks under sustained load: {clocks}")
     tflops = w.flop / (ms_step * 1e-3) / 1e12
     kernel_tflops = w.flop / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -205,7 +252,9 @@ def main():
     secondary = {}
     if not args.no_secondary:
         # (workload, B layout, kernel config, split-K parts or None for the plain entry point)
-        runs = [("square_1024", binding.B_KN, binding.CONFIG_AUTO, None),
+        runs = [("small_256", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("square_1024", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, None),     # the pages' 128x128x64 tile
                 ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, 4),
                 ("ragged_4000x11000x4100", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, None),
@@ -219,7 +268,7 @@ def main():
             if (sw.name == w.name and s_splits is None and s_config == binding.CONFIG_AUTO and
                     args.b_layout == ("nk" if b_layout == binding.B_NK else "kn")):
                 continue
-            s_ms, s_kms = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, config=s_config,
+            s_ms, s_kms, _ = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, config=s_config,
                                         b_layout=b_layout, splits=s_splits)
             if b_layout == binding.B_NK:
                 name += "_b_nk"
@@ -264,6 +313,7 @@ def main():
                      "traffic": (measured_traffic(w.name, binding.CONFIG_NAMES.get(cfg["config_id"]))
                                  if b_layout == binding.B_KN else None)},
         "cpu_baseline": cpu,
+        "clocks": clocks,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

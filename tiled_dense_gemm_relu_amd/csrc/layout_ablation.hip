@@ -1,0 +1,112 @@
+// Layout ablation: the 256x256x32 LDS-DMA kernel with and without the XOR
+// swizzle of its LDS rows, on ReLU(A @ B) 8192^3 fp16 (entries N(0, 0.1^2)).
+//
+// The pages report that swizzling the shared-memory layout cut the share of
+// kernel time spent in shared-memory reads from 41% to 17% (the zwxr.cn
+// hands-on TileLang article, section 2.3, hardware not stated).  This program
+// measures the same switch on gfx950: both variants run in one process,
+// alternating, and must give bit-identical C.  Run it under
+//   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE ... -- ./layout_ablation
+// for the bank-conflict counters of each variant (the kernels differ in their
+// DmaConfig's last template argument).
+//
+// Output: one JSON line per round, then {"outputs_identical": ...}.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "gemm_relu_kernels.hpp"
+
+namespace {
+
+using namespace gemm_relu_hip;
+using Swizzled = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 16, false, 0, true>;
+using Plain = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 16, false, 0, false>;
+
+#define CHECK(x)                                                                               \
+    do {                                                                                       \
+        hipError_t e_ = (x);                                                                   \
+        if (e_ != hipSuccess) {                                                                \
+            std::fprintf(stderr, "%s failed: %s (line %d)\n", #x, hipGetErrorString(e_), __LINE__); \
+            std::exit(1);                                                                      \
+        }                                                                                      \
+    } while (0)
+
+template <class Cfg>
+float time_kernel(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K, int cus, int reps)
+{
+    int tiles_m = (M + Cfg::BM - 1) / Cfg::BM, tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+    const int grid = std::min(tiles_m * tiles_n, cus);
+    int c_vec_ok = 1, splits = 1;
+    float* ws = nullptr;
+    int* counters = nullptr;
+    void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &c_vec_ok, &ws, &counters, &splits};
+    const void* fn = (const void*)&gemm_relu_dma<Cfg, kF16, false>;
+    for (int i = 0; i < 3; ++i) CHECK(hipLaunchKernel(fn, dim3(grid), dim3(Cfg::THREADS), args, 0, nullptr));
+    hipEvent_t t0, t1;
+    CHECK(hipEventCreate(&t0));
+    CHECK(hipEventCreate(&t1));
+    CHECK(hipEventRecord(t0, nullptr));
+    for (int i = 0; i < reps; ++i) CHECK(hipLaunchKernel(fn, dim3(grid), dim3(Cfg::THREADS), args, 0, nullptr));
+    CHECK(hipEventRecord(t1, nullptr));
+    CHECK(hipEventSynchronize(t1));
+    float ms = 0.0f;
+    CHECK(hipEventElapsedTime(&ms, t0, t1));
+    CHECK(hipEventDestroy(t0));
+    CHECK(hipEventDestroy(t1));
+    return ms / reps;
+}
+
+}  // namespace
+
+int main()
+{
+    const int M = 8192, N = 8192, K = 8192, rounds = 4, reps = 30;
+    int dev = 0;
+    hipDeviceProp_t prop;
+    CHECK(hipGetDevice(&dev));
+    CHECK(hipGetDeviceProperties(&prop, dev));
+    if (std::string(prop.gcnArchName).rfind("gfx950", 0) != 0) {
+        std::fprintf(stderr, "needs a gfx950 GPU, found %s\n", prop.gcnArchName);
+        return 2;
+    }
+    // Row-major A (M x K) and B (K x N), fp16 N(0, 0.1^2); the shapes match the
+    // kernel's tiles exactly, so no tail instance is needed.
+    std::vector<_Float16> host((size_t)M * K);
+    std::mt19937 rng(1003);
+    std::normal_distribution<float> normal(0.0f, 0.1f);
+    uint16_t *A = nullptr, *B = nullptr, *C1 = nullptr, *C2 = nullptr;
+    CHECK(hipMalloc(&A, (size_t)M * K * 2));
+    CHECK(hipMalloc(&B, (size_t)K * N * 2));
+    CHECK(hipMalloc(&C1, (size_t)M * N * 2));
+    CHECK(hipMalloc(&C2, (size_t)M * N * 2));
+    for (auto& x : host) x = (_Float16)normal(rng);
+    CHECK(hipMemcpy(A, host.data(), host.size() * 2, hipMemcpyHostToDevice));
+    for (auto& x : host) x = (_Float16)normal(rng);
+    CHECK(hipMemcpy(B, host.data(), host.size() * 2, hipMemcpyHostToDevice));
+
+    const double flop = 2.0 * M * N * K;
+    for (int r = 0; r < rounds; ++r) {
+        const float ts = time_kernel<Swizzled>(A, B, C1, M, N, K, prop.multiProcessorCount, reps);
+        const float tp = time_kernel<Plain>(A, B, C2, M, N, K, prop.multiProcessorCount, reps);
+        std::printf("{\"round\": %d, \"swizzled_ms\": %.4f, \"swizzled_tflops\": %.1f, \"unswizzled_ms\": %.4f, "
+                    "\"unswizzled_tflops\": %.1f}\n",
+                    r, ts, flop / ts / 1e9, tp, flop / tp / 1e9);
+        std::fflush(stdout);
+    }
+    std::vector<uint16_t> c1((size_t)M * N), c2((size_t)M * N);
+    CHECK(hipMemcpy(c1.data(), C1, c1.size() * 2, hipMemcpyDeviceToHost));
+    CHECK(hipMemcpy(c2.data(), C2, c2.size() * 2, hipMemcpyDeviceToHost));
+    const bool same = c1 == c2;
+    std::printf("{\"outputs_identical\": %s}\n", same ? "true" : "false");
+    CHECK(hipFree(A));
+    CHECK(hipFree(B));
+    CHECK(hipFree(C1));
+    CHECK(hipFree(C2));
+    return same ? 0 : 1;
+}
