@@ -162,6 +162,35 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     return total_ms / steps, kernel_ms, clocks
 
 
+def time_vendor(w, steps, warmup, n_sets, device):
+    """The same workload through the vendor library in one process: torch.mm (hipBLASLt on
+    ROCm) alone, and followed by an in-place ReLU (two kernels).  Mean ms per step between GPU
+    events.  For context only: nothing in the library uses it."""
+    sets = make_sets(w, n_sets, device)
+    stream = torch.cuda.current_stream(device)
+    out = {}
+    for name, relu in (("mm_ms", False), ("mm_relu_ms", True)):
+        def step(i):
+            a, b, c = sets[i % n_sets]
+            torch.mm(a, b, out=c)
+            if relu:
+                torch.relu_(c)
+        for i in range(warmup):
+            step(i)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(device)
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize(device)
+        out[name] = round(t0.elapsed_time(t1) / steps, 5)
+    out["mm_tflops"] = round(w.flop / (out["mm_ms"] * 1e-3) / 1e12, 1)
+    out["mm_relu_tflops"] = round(w.flop / (out["mm_relu_ms"] * 1e-3) / 1e12, 1)
+    del sets
+    return out
+
+
 def cpu_baseline(w, target_s):
     """The CPU oracle on a bounded sample of the workload: whole rows of C."""
     import oracle
@@ -215,6 +244,8 @@ def main():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
+    p.add_argument("--no-vendor", action="store_true",
+                   help="skip timing the same workload through torch.mm (+ torch.relu_)")
     p.add_argument("--clock-seconds", type=float, default=2.0,
                    help="after the timed steps, sustain the workload this long while rocm-smi samples the "
                         "shader clock (0: skip)")
@@ -283,6 +314,12 @@ def main():
             secondary[name] = entry
             log(f"[bench] {name}: {entry}")
 
+    vendor = None
+    if not args.no_vendor:
+        vendor = time_vendor(w, args.steps, args.warmup, args.sets, device)
+        vendor["fused_kernel_vs_mm_relu"] = round(vendor["mm_relu_ms"] / ms_step, 3)
+        log(f"[bench] vendor library (torch.mm, then torch.relu_): {vendor}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
@@ -314,6 +351,7 @@ def main():
                                  if b_layout == binding.B_KN else None)},
         "cpu_baseline": cpu,
         "clocks": clocks,
+        "vendor_reference": vendor,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
