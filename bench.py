@@ -49,7 +49,7 @@ def measured_traffic(workload_name, kernel_name):
             prof = json.load(f)
     except (OSError, ValueError):
         return None
-    if not prof.get("workload", "").startswith(workload_name) or kernel_name != "dma_256x256x32_4stage":
+    if not prof.get("workload", "").startswith(workload_name) or kernel_name != "dma_256x256x64_2stage":
         return None
     if prof.get("kernel_source_sha256") != kernel_source_digest():
         return None

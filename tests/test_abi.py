@@ -102,8 +102,8 @@ def test_k_zero_needs_no_inputs():
 
 def test_config_choice_for_the_workload_shapes():
     big = gr.selected_config(8192, 8192, 8192)
-    assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (3, 256, 256, 32)
-    assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (4, 8, 8, 1024, 131072)
+    assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (3, 256, 256, 64)
+    assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (2, 8, 8, 1024, 131072)
     small = gr.selected_config(1024, 1024, 1024)
     assert (small["config_id"], small["block_m"], small["stages"], small["grid"]) == (5, 64, 8, 256)
     mid = gr.selected_config(2048, 2048, 2048)

@@ -190,7 +190,9 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 
     if (chosen >= GEMM_RELU_CONFIG_DMA_256) {
         const int id = chosen - GEMM_RELU_CONFIG_DMA_256;
-        const TileGeom& g = kDmaGeom[id];
+        // 4-byte DMA lanes (256 tile only) use their own stage geometry.
+        const bool dword = id == kDma256 && (plan->b_nk ? !full_vectors : (va < 8 || vb < 8));
+        const TileGeom& g = dword ? kDma256DwGeom : kDmaGeom[id];
         const int64_t b_band = plan->b_nk ? int64_t(g.bn) * K * 2 : int64_t(g.bk) * N * 2;
         if (int64_t(g.bm) * K * 2 > kMaxBand || b_band > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
         const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
@@ -322,7 +324,7 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
         float* ws = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.counter_bytes)
                                  : nullptr;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok, &ws, &counters, &splits};
-        const int ktail = K % kDmaGeom[p.dma_id].bk != 0 ? 1 : 0;
+        const int ktail = K % p.cfg.block_k != 0 ? 1 : 0;
         const void* fn = p.splits > 1 ? ks.splitk[p.b_nk][p.dma_id][ktail]
                        : p.b_nk ? (p.dma_id == kDma256 && p.dma_a4 ? ks.dma256_nt_dw[ktail] : ks.dma_nt[p.dma_id][ktail])
                        : p.dma_id == kDma256 ? ks.dma256_dw[p.dma_a4][p.dma_b4][ktail]

@@ -18,9 +18,16 @@ template <class Cfg, int id>
 constexpr bool dma_geom_matches = Cfg::BM == kDmaGeom[id].bm && Cfg::BN == kDmaGeom[id].bn &&
                                   Cfg::BK == kDmaGeom[id].bk && Cfg::STAGES == kDmaGeom[id].stages &&
                                   Cfg::THREADS == kDmaGeom[id].threads && Cfg::GROUP_M == kDmaGeom[id].group_m;
+template <class Cfg>
+constexpr bool dw_geom_matches = Cfg::BM == kDma256DwGeom.bm && Cfg::BN == kDma256DwGeom.bn &&
+                                 Cfg::BK == kDma256DwGeom.bk && Cfg::STAGES == kDma256DwGeom.stages &&
+                                 Cfg::THREADS == kDma256DwGeom.threads && Cfg::GROUP_M == kDma256DwGeom.group_m;
+static_assert(dw_geom_matches<DmaTile256A4> && dw_geom_matches<DmaTile256B4> && dw_geom_matches<DmaTile256AB4> &&
+                  dw_geom_matches<DmaTile256T4>,
+              "host geometry of the 4-byte-lane 256 instances out of date");
 static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
                   dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
-                  dma_geom_matches<DmaTile256T4, kDma256> && dma_geom_matches<DmaTile128T, kDma128> &&
+                  dma_geom_matches<DmaTile128T, kDma128> &&
                   dma_geom_matches<DmaTile64T, kDma64> && dma_geom_matches<DmaTile64x256, kDma64x256> &&
                   dma_geom_matches<DmaTile64x256T, kDma64x256> && dma_geom_matches<DmaTile256x128W, kDma256x128W> &&
                   dma_geom_matches<DmaTile256x128WT, kDma256x128W>,

@@ -1,4 +1,4 @@
-// Layout ablation: the 256x256x32 LDS-DMA kernel with and without the XOR
+// Layout ablation: the 256x256x64 LDS-DMA kernel with and without the XOR
 // swizzle of its LDS rows, on ReLU(A @ B) 8192^3 fp16 (entries N(0, 0.1^2)).
 //
 // The pages report that swizzling the shared-memory layout cut the share of
@@ -25,8 +25,8 @@
 namespace {
 
 using namespace gemm_relu_hip;
-using Swizzled = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 16, false, 0, true>;
-using Plain = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 16, false, 0, false>;
+using Swizzled = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true>;
+using Plain = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, false>;
 
 #define CHECK(x)                                                                               \
     do {                                                                                       \
