@@ -1,0 +1,51 @@
+"""Host-side checks of the offline tile-configuration search (no GPU: the
+candidate enumeration is pure configuration queries, and the table writer is
+plain text)."""
+import re
+
+import tiled_dense_gemm_relu_amd as gr
+from tiled_dense_gemm_relu_amd import tune
+
+
+def test_parse_shape():
+    assert tune.parse_shape("64,16384,8192,bf16,nk") == (64, 16384, 8192, "bf16", 1)
+    assert tune.parse_shape("512,512,512") == (512, 512, 512, "fp16", 0)
+
+
+def test_default_shapes_cover_the_workloads_in_both_layouts():
+    shapes = tune.default_shapes()
+    assert (8192, 8192, 8192, "fp16", 0) in shapes and (8192, 8192, 8192, "fp16", 1) in shapes
+    assert (64, 16384, 8192, "bf16", 0) in shapes
+    assert len(set(shapes)) == len(shapes)
+
+
+def test_candidates_are_distinct_resolved_configurations():
+    cands = tune.candidates(512, 512, 16384, gr.F16, gr.B_KN)
+    assert len(cands) == len(set(cands))
+    assert all(0 <= c <= 7 and 1 <= s <= 16 for c, s in cands)
+    assert (5, 4) in cands and (3, 1) in cands           # split-K on the 64 tile, the 256 tile
+    assert (0, 1) not in cands                           # the direct kernel only when nothing else runs
+    # every candidate is what the library resolves a request to
+    for c, s in cands:
+        r = gr.selected_splitk_config(512, 512, 16384, config=c, splits=s) if s > 1 else \
+            gr.selected_config(512, 512, 16384, config=c)
+        assert (r["config_id"], r["splits"]) == (c, s)
+    # odd K: only the kernels that take 2-byte loads remain, the direct kernel among them for B (N, K)
+    assert tune.candidates(100, 100, 101, gr.F16, gr.B_NK) == [(0, 1)]
+
+
+def test_split_candidates_respect_the_workspace_cap():
+    for c, s in tune.candidates(8192, 8192, 8192, gr.F16, gr.B_KN):
+        if s > 1:
+            assert gr.selected_splitk_config(8192, 8192, 8192, config=c, splits=s)["workspace_bytes"] <= \
+                tune.MAX_WORKSPACE
+
+
+def test_write_table_round_trips(tmp_path):
+    entries = [{"M": 8, "N": 16, "K": 24, "dtype": "bf16", "b_layout": 1, "config": 5, "splitk_config": 6,
+                "splits": 4}]
+    path = tmp_path / "t.inc"
+    tune.write_table(entries, "test device", str(path))
+    rows = [tuple(int(v) for v in m.group(1).split(","))
+            for m in (re.match(r"\{(.*)\},\s*$", l.strip()) for l in path.read_text().splitlines()) if m]
+    assert rows == [(8, 16, 24, 1, 1, 5, 6, 4)]
