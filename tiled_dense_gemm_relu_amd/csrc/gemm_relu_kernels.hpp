@@ -623,8 +623,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const uint32_t b_stage_bytes = (uint32_t)BK * (uint32_t)N * 2u;
 
     // The load side of the stream: the unit and K-step the next DMA belongs to.
+    // Past the end of the stream the descriptors are zero-length (f_b_bytes =
+    // 0 for B stored (K, N)), so the remaining ring steps fetch nothing
+    // without a per-instruction test.
     int f_unit = 0, f_kt = 0, f_kt_end = 0, f_m0 = 0, f_n0 = 0;
     int32x4_t f_rsrc_a = rsrc_none, f_rsrc_bt = rsrc_none;
+    const uint16_t* f_b_ptr = B;   // B stored (K, N): element (k0, f_n0) of the current step
+    uint32_t f_b_bytes = 0;        // ... and the bytes its descriptor covers (a whole stage)
     auto fill_tile_setup = [&]() {
         if (f_unit < n_units) {
             int tile, part;
@@ -636,7 +641,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             if constexpr (Cfg::B_KMAJOR) {   // rows f_n0 .. of B^T; rows past N read as zero
                 const int valid_n = min(BN, N - f_n0);
                 f_rsrc_bt = rsrc_words(B + (size_t)f_n0 * (size_t)K, (uint32_t)valid_n * (uint32_t)K * 2u);
+            } else {
+                f_b_ptr = B + (size_t)f_kt * BK * (size_t)N + f_n0;
+                f_b_bytes = b_stage_bytes;
             }
+        } else {
+            f_rsrc_a = f_rsrc_bt = rsrc_none;
+            f_b_bytes = 0u;
         }
     };
     fill_tile_setup();
@@ -650,15 +661,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // descriptor: nothing is fetched.
     auto dma = [&](int slot, int q) {
         const int k0 = f_kt * BK;
-        const bool live = f_unit < n_units;
         if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
             if (KTAIL) {   // pieces past K read as zero (K is a multiple of the piece length)
                 vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
                 so = 0u;
             }
-            dma_issue(live ? f_rsrc_a : rsrc_none, lds_base + slot * Cfg::A_STAGE + (dwave * QA + q) * 64 * LA, vo,
-                      live ? so : 0u, LA);
+            dma_issue(f_rsrc_a, lds_base + slot * Cfg::A_STAGE + (dwave * QA + q) * 64 * LA, vo, so, LA);
         } else if constexpr (Cfg::B_KMAJOR) {
             const int qb = q - QA;
             uint32_t vo = b_voff[qb], so = (uint32_t)k0 * 2u;
@@ -666,12 +675,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                 vo = k0 + b_ncol[qb] < K ? b_voff[qb] + so : kOobOffset;
                 so = 0u;
             }
-            dma_issue(live ? f_rsrc_bt : rsrc_none, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (dwave * QB + qb) * 64 * LB,
-                      vo, live ? so : 0u, LB);
+            dma_issue(f_rsrc_bt, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (dwave * QB + qb) * 64 * LB, vo, so,
+                      LB);
         } else {
             // descriptor based at (row k0, column f_n0): rows past K read as zero
-            const uint32_t nb = KTAIL ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : b_stage_bytes;
-            const int32x4_t rb = live ? rsrc_words(B + (size_t)k0 * (size_t)N + f_n0, nb) : rsrc_none;
+            const uint32_t nb =
+                KTAIL ? (f_b_bytes ? (uint32_t)min(BK, K - k0) * (uint32_t)N * 2u : 0u) : f_b_bytes;
+            const int32x4_t rb = rsrc_words(f_b_ptr, nb);
             const uint32_t vo = f_n0 + b_ncol[q - QA] < N ? b_voff[q - QA] : kOobOffset;   // columns past N
             dma_issue(rb, lds_base + Cfg::B_REGION + slot * Cfg::B_STAGE + (dwave * QB + (q - QA)) * 64 * LB, vo, 0u,
                       LB);
@@ -681,6 +691,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         if (++f_kt == f_kt_end) {
             ++f_unit;
             fill_tile_setup();
+        } else if constexpr (!Cfg::B_KMAJOR) {
+            f_b_ptr += (size_t)BK * (size_t)N;
         }
     };
 
