@@ -293,6 +293,7 @@ def main():
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
                 ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None),
+                ("square_8192_bf16", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("square_8192", binding.B_KN, binding.CONFIG_DMA_256x128_WS, None)]
         for name, b_layout, s_config, s_splits in runs:
             sw = inputs.WORKLOADS[name]

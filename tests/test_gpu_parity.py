@@ -155,9 +155,10 @@ def test_ragged_4000x11000x4100_sampled(integer):
         assert 0.4 < frac_zero < 0.6                # about half the sums are negative
 
 
+@pytest.mark.parametrize("name", ["square_8192", "square_8192_bf16"])
 @pytest.mark.parametrize("integer", [False, True])
-def test_square_8192_sampled(integer):
-    w = inputs.WORKLOADS["square_8192"]
+def test_square_8192_sampled(integer, name):
+    w = inputs.WORKLOADS[name]
     got = check_sampled(w, integer, n_entries=1024)
     if not integer:
         assert 0.45 < (got == 0).mean() < 0.55

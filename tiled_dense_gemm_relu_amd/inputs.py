@@ -52,8 +52,8 @@ class Workload:
 
 # The workload shapes: a small correctness case, the 1024^3 example shape with
 # 128x128x64 tiles, the 8192^3 compute-bound headline, a shape with ragged M, N
-# and K tails, a skinny decode-like bf16 shape that is HBM-bound, and a deep-K
-# shape with few output tiles.
+# and K tails, a skinny decode-like bf16 shape that is HBM-bound, a deep-K
+# shape with few output tiles, and the headline shape in bf16.
 WORKLOADS = {
     "small_256": Workload("small_256", 256, 256, 256, "fp16", 1.0, 1001, 1011),
     "square_1024": Workload("square_1024", 1024, 1024, 1024, "fp16", 1.0, 1002, 1012),
@@ -64,6 +64,8 @@ WORKLOADS = {
                                      1005, 1015),
     # few output tiles over a long K: the case split-K is for
     "deep_512x512x16384": Workload("deep_512x512x16384", 512, 512, 16384, "fp16", 0.05, 1006, 1016),
+    # the headline shape in bf16
+    "square_8192_bf16": Workload("square_8192_bf16", 8192, 8192, 8192, "bf16", 0.1, 1007, 1017),
 }
 
 
