@@ -22,7 +22,9 @@
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL means the null
  * stream) and the call returns without waiting.  C is complete once the
  * stream has been synchronised.  Calls on different streams that write the
- * same C race.
+ * same C race.  Every entry point enqueues kernel launches only (no memset, no
+ * copy, no allocation), so calls can be captured into a HIP graph and replayed;
+ * the first call on a device queries its properties, so make it before capture.
  *
  * Errors: every argument is checked before anything is launched; on an error
  * the return value is negative, nothing is launched and C is not touched.

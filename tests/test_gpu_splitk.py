@@ -156,3 +156,24 @@ def test_splitk_deep_512x512x16384_full(integer):
         assert np.array_equal(got, want)
     else:
         assert_within_tolerance(got, want, w.dtype)
+
+
+def test_splitk_on_two_streams_uses_two_workspaces():
+    # The binding keeps one cached workspace per stream: two streams running
+    # split-K at the same time never share counters or partials.
+    M, N, K = 64, 4096, 4096
+    pairs = [inputs.integer_pair(M, N, K, torch.float16, seed=s) for s in (31, 32)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    dev_pairs = [(a.cuda(), b.cuda()) for a, b in pairs]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for (a, b), st in zip(dev_pairs, streams):
+            with torch.cuda.stream(st):
+                outs.append(gr.gemm_relu_splitk(a, b, config=binding.CONFIG_DMA_64x256, splits=8))
+    torch.cuda.synchronize()
+    for i, c in enumerate(outs):
+        a, b = pairs[i % 2]
+        assert np.array_equal(bits(c), oracle.gemm_relu(a, b, "fp16")), i
+    keys = [k for k in binding._workspaces if k[1] in (streams[0].cuda_stream, streams[1].cuda_stream)]
+    assert len(keys) == 2
