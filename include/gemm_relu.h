@@ -121,7 +121,7 @@ typedef struct {
     int vec_b;        /* elements per global load of B */
     int64_t grid;     /* output tiles; workgroups launched, except for the DMA_* kernels, which
                          run one persistent workgroup per CU (at most one per tile) */
-    int lds_bytes;    /* LDS per workgroup */
+    int lds_bytes;    /* LDS per workgroup: the ring of stages, plus C staging for the LDS-DMA kernels */
     int b_layout;     /* GEMM_RELU_B_KN or GEMM_RELU_B_NK */
     int splits;       /* K parts per output tile (1: no split-K) */
     int64_t workspace_bytes;   /* split-K workspace needed (0 when splits == 1) */

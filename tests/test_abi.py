@@ -103,7 +103,8 @@ def test_k_zero_needs_no_inputs():
 def test_config_choice_for_the_workload_shapes():
     big = gr.selected_config(8192, 8192, 8192)
     assert (big["config_id"], big["block_m"], big["block_n"], big["block_k"]) == (3, 256, 256, 64)
-    assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (2, 8, 8, 1024, 131072)
+    # the 128 KiB ring plus 8 waves x 4 KiB of C staging: the whole 160 KiB
+    assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (2, 8, 8, 1024, 163840)
     small = gr.selected_config(1024, 1024, 1024)
     assert (small["config_id"], small["block_m"], small["stages"], small["grid"]) == (5, 64, 8, 256)
     mid = gr.selected_config(2048, 2048, 2048)
@@ -257,7 +258,7 @@ def test_tuned_table_needs_the_tuners_alignment():
 def test_wave_specialised_config():
     cfg = gr.selected_config(8192, 8192, 8192, config=7)
     assert (cfg["config_id"], cfg["block_m"], cfg["block_n"], cfg["block_k"], cfg["threads"]) == (7, 256, 128, 32, 768)
-    assert (cfg["grid"], cfg["lds_bytes"]) == (32 * 64, 4 * 384 * 32 * 2)
+    assert (cfg["grid"], cfg["lds_bytes"]) == (32 * 64, 4 * 384 * 32 * 2 + 8 * 4096)
     assert gr.selected_config(8192, 8192, 8192, config=7, b_layout=gr.B_NK)["config_id"] == 7
     # needs 16-byte loads: else the 256 tile of the layout's fallback family
     assert gr.selected_config(512, 512, 516, config=7)["config_id"] == 1

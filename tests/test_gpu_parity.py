@@ -245,6 +245,27 @@ def test_nothing_written_outside_c(config):
     assert_within_tolerance(raw[guard:guard + M * N].reshape(M, N), oracle.gemm_relu(a, b, "fp16"), "fp16")
 
 
+@pytest.mark.parametrize("c_off", [0, 4, 2, 1])
+@pytest.mark.parametrize("config", CONFIGS)
+def test_c_store_paths(c_off, config):
+    # N % 8 == 0 with M and N tails.  C starting c_off elements into a buffer
+    # selects the store path: 0 gives 16-byte aligned rows (16-byte pieces; the
+    # LDS-DMA kernels stage them through LDS), 4 gives 8-byte pieces, and 2
+    # and 1 give element stores.  NaN guards on both sides must survive.
+    M, N, K = 300, 264, 96
+    guard = 4096
+    a, b = inputs.integer_pair(M, N, K, torch.float16, seed=300 + c_off)
+    want = oracle.gemm_relu(a, b, "fp16")
+    buf = torch.full((M * N + 2 * guard + c_off,), float("nan"), dtype=torch.float16, device="cuda")
+    c = buf[guard + c_off:guard + c_off + M * N].view(M, N)
+    gr.gemm_relu(a.cuda(), b.cuda(), out=c, config=config)
+    torch.cuda.synchronize()
+    raw = bits(buf)
+    nan_bits = bits(torch.tensor([float("nan")], dtype=torch.float16))[0]
+    assert (raw[:guard + c_off] == nan_bits).all() and (raw[guard + c_off + M * N:] == nan_bits).all()
+    assert np.array_equal(raw[guard + c_off:guard + c_off + M * N].reshape(M, N), want)
+
+
 def test_run_to_run_bit_identical():
     w = inputs.WORKLOADS["ragged_4000x11000x4100"]
     a, b = inputs.workload_inputs(w)

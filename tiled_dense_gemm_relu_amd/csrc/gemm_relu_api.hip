@@ -123,7 +123,8 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)) return GEMM_RELU_ERR_ALIAS;
 
     const uintptr_t c_addr = reinterpret_cast<uintptr_t>(C);
-    plan->c_vec_ok = (N % 4 == 0 && c_addr % 8 == 0) ? 1 : 0;
+    // 2: 16-byte pieces of C rows (the LDS-DMA kernels' staged stores), 1: 8-byte pieces, 0: elements.
+    plan->c_vec_ok = (N % 8 == 0 && c_addr % 16 == 0) ? 2 : (N % 4 == 0 && c_addr % 8 == 0) ? 1 : 0;
 
     if (K == 0) {
         plan->tile = -2;
@@ -212,7 +213,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         plan->cfg.vec_a = plan->dma_a4 ? 2 : 8;
         plan->cfg.vec_b = plan->dma_b4 ? 2 : 8;
         plan->cfg.grid = tm * tn;
-        plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2;
+        plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2 + g.c_stage;
         if (splits_req >= 0 && has_splitk(id)) {
             const int64_t tiles = tm * tn, kt = ceil_div(K, g.bk);
             int64_t s = splits_req;

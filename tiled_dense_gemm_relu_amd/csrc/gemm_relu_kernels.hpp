@@ -180,6 +180,50 @@ __device__ __forceinline__ void store_block(uint16_t* __restrict__ C, const floa
     }
 }
 
+// Store one wave's output, FN x FM blocks as store_block takes them (block
+// (i, j) covers rows m_base + 32j .. +31 and columns n_base + 32i .. +31),
+// through the wave's 4 KiB LDS strip.  Per round, blocks (2p, j) and (2p+1, j),
+// 32 rows x 64 columns, are ReLU'd, rounded and written to the strip; then
+// each row piece is read back and stored as 16-byte pieces, 8 lanes per
+// 128-byte row piece, instead of 8-byte pieces of 32 different rows.  Strip
+// rows are 128 bytes, and 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7): the 8-byte writes (32 rows at one chunk) take the
+// minimum two LDS passes and the 16-byte reads are conflict-free.  A wave's
+// LDS accesses complete in order, so one round's reads finish before the
+// next round's writes reuse the strip.  Needs N % 8 == 0 and a 16-byte
+// aligned C; rows past M and pieces past N are skipped.
+template <int DT, int FN, int FM>
+__device__ __forceinline__ void store_tile_staged(uint16_t* __restrict__ C, const floatx16 (&acc)[FN][FM],
+                                                  uint8_t* strip, int lane, int m_base, int n_base, int M, int N)
+{
+    static_assert(FN % 2 == 0, "pairs of 32-column blocks");
+    const int rw = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int p = 0; p < FN / 2; ++p) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // lane l, registers 4q .. 4q+3: row l % 32, columns 32ii + 8q + 4(l / 32) + 0..3
+                    const floatx16& a = acc[2 * p + ii][j];
+                    const uint32_t lo = (uint32_t)relu_cast<DT>(a[4 * q]) | ((uint32_t)relu_cast<DT>(a[4 * q + 1]) << 16);
+                    const uint32_t hi =
+                        (uint32_t)relu_cast<DT>(a[4 * q + 2]) | ((uint32_t)relu_cast<DT>(a[4 * q + 3]) << 16);
+                    *reinterpret_cast<u32x2*>(strip + rw * 128 + (((4 * ii + q) ^ ((rw >> 1) & 7)) << 4) + 8 * h) =
+                        u32x2{lo, hi};
+                }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int r = 8 * s + (lane >> 3), c = lane & 7;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(strip + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+                const int m = m_base + 32 * j + r, n = n_base + 64 * p + 8 * c;
+                if (m < M && n < N) *reinterpret_cast<u32x4*>(C + (size_t)m * (size_t)N + n) = v;
+            }
+        }
+}
+
 // ---------------------------------------------------------------- tiled kernel
 
 // BM x BN x 64 block tile, WAVES_M x WAVES_N waves, two LDS stages with the
@@ -498,6 +542,13 @@ struct DmaConfig {
     static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * BK * 2;          // bytes per stage
     static constexpr int B_REGION = STAGES * A_STAGE;                // B stages follow the A stages
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+    // C staging: each compute wave writes its finished output through a
+    // private 4 KiB LDS strip past the ring (two 32x32 blocks at a time), so
+    // that C leaves as whole 128-byte row pieces.  Needs an even number of
+    // 32-column blocks per wave and room in the 160 KiB; else 0 and C is
+    // stored straight from the accumulators.
+    static constexpr int C_STAGE_WAVE = (FN % 2 == 0 && LDS_BYTES + WAVES * 4096 <= 160 * 1024) ? 4096 : 0;
+    static constexpr int C_STAGE_BYTES = WAVES * C_STAGE_WAVE;
     // Bytes each lane moves per DMA instruction: 16 (buffer_load_dwordx4, needs
     // rows of a multiple of 8 elements) or 4 (buffer_load_dword, rows of an even
     // number of elements).
@@ -539,7 +590,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     constexpr int QA = Cfg::QA, QB = Cfg::QB, NQ = Cfg::NQ, FM = Cfg::FM, FN = Cfg::FN;
     constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN, NKS = Cfg::NKS;
     constexpr int A_ROW = Cfg::A_ROW, B_ROW = Cfg::B_ROW;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES + Cfg::C_STAGE_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -916,12 +967,22 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                 if (splits > 1) store = combine_parts(acc);
             }
             if (store) {
+                bool staged = false;
+                if constexpr (Cfg::C_STAGE_WAVE > 0) {
+                    if (c_vec_ok == 2) {
+                        store_tile_staged<DT>(C, acc, smem + Cfg::LDS_BYTES + wave * Cfg::C_STAGE_WAVE, lane,
+                                              c_m0 + wm * WTM, c_n0 + wn * WTN, M, N);
+                        staged = true;
+                    }
+                }
+                if (!staged) {
 #pragma unroll
-                for (int i = 0; i < FN; ++i)
+                    for (int i = 0; i < FN; ++i)
 #pragma unroll
-                    for (int j = 0; j < FM; ++j)
-                        store_block<DT>(C, acc[i][j], lane, c_m0 + wm * WTM + j * 32, c_n0 + wn * WTN + i * 32, M,
-                                        N, c_vec_ok != 0);
+                        for (int j = 0; j < FM; ++j)
+                            store_block<DT>(C, acc[i][j], lane, c_m0 + wm * WTM + j * 32, c_n0 + wn * WTN + i * 32,
+                                            M, N, c_vec_ok != 0);
+                }
             }
 #pragma unroll
             for (int i = 0; i < FN; ++i)

@@ -11,6 +11,7 @@ enum TileId { kTile256 = 0, kTile128 = 1, kNumTiles = 2 };
 // Geometry of each tile configuration (must match the TileConfig instances).
 struct TileGeom {
     int bm, bn, bk, stages, threads, group_m;
+    int c_stage = 0;   // LDS bytes past the ring for staging C (LDS-DMA kernels)
 };
 constexpr TileGeom kTileGeom[kNumTiles] = {
     {256, 256, 64, 2, 256, 8},
@@ -44,16 +45,16 @@ enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W 
 // Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64 / DmaTile64x256 /
 // DmaTile256x128W; threads include the producer waves).
 constexpr TileGeom kDmaGeom[kNumDma] = {
-    {256, 256, 64, 2, 512, 4},
-    {128, 128, 64, 4, 256, 4},
-    {64, 64, 64, 8, 256, 4},
-    {64, 256, 32, 8, 256, 4},
-    {256, 128, 32, 4, 768, 4},
+    {256, 256, 64, 2, 512, 4, 32768},
+    {128, 128, 64, 4, 256, 4, 16384},
+    {64, 64, 64, 8, 256, 4, 0},
+    {64, 256, 32, 8, 256, 4, 0},
+    {256, 128, 32, 4, 768, 4, 32768},
 };
 // The 256 instances with 4-byte DMA lanes keep BK = 32 in 4 stages: with their
 // twice as many DMA instructions, the deeper ring measured faster (the ragged
 // 4000x11000x4100 shape: about 4%).
-constexpr TileGeom kDma256DwGeom = {256, 256, 32, 4, 512, 4};
+constexpr TileGeom kDma256DwGeom = {256, 256, 32, 4, 512, 4, 32768};
 
 const DtypeKernels& kernels_f16();
 const DtypeKernels& kernels_bf16();

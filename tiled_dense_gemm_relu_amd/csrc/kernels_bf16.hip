@@ -17,11 +17,13 @@ static_assert(geom_matches<Tile256, kTile256> && geom_matches<Tile128, kTile128>
 template <class Cfg, int id>
 constexpr bool dma_geom_matches = Cfg::BM == kDmaGeom[id].bm && Cfg::BN == kDmaGeom[id].bn &&
                                   Cfg::BK == kDmaGeom[id].bk && Cfg::STAGES == kDmaGeom[id].stages &&
-                                  Cfg::THREADS == kDmaGeom[id].threads && Cfg::GROUP_M == kDmaGeom[id].group_m;
+                                  Cfg::THREADS == kDmaGeom[id].threads && Cfg::GROUP_M == kDmaGeom[id].group_m &&
+                                  Cfg::C_STAGE_BYTES == kDmaGeom[id].c_stage;
 template <class Cfg>
 constexpr bool dw_geom_matches = Cfg::BM == kDma256DwGeom.bm && Cfg::BN == kDma256DwGeom.bn &&
                                  Cfg::BK == kDma256DwGeom.bk && Cfg::STAGES == kDma256DwGeom.stages &&
-                                 Cfg::THREADS == kDma256DwGeom.threads && Cfg::GROUP_M == kDma256DwGeom.group_m;
+                                 Cfg::THREADS == kDma256DwGeom.threads && Cfg::GROUP_M == kDma256DwGeom.group_m &&
+                                 Cfg::C_STAGE_BYTES == kDma256DwGeom.c_stage;
 static_assert(dw_geom_matches<DmaTile256A4> && dw_geom_matches<DmaTile256B4> && dw_geom_matches<DmaTile256AB4> &&
                   dw_geom_matches<DmaTile256T4>,
               "host geometry of the 4-byte-lane 256 instances out of date");

@@ -42,7 +42,7 @@ float time_kernel(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int 
 {
     int tiles_m = (M + Cfg::BM - 1) / Cfg::BM, tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
     const int grid = std::min(tiles_m * tiles_n, cus);
-    int c_vec_ok = 1, splits = 1;
+    int c_vec_ok = 2, splits = 1;   // N % 8 == 0 and hipMalloc alignment: 16-byte C pieces
     float* ws = nullptr;
     int* counters = nullptr;
     void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &c_vec_ok, &ws, &counters, &splits};
