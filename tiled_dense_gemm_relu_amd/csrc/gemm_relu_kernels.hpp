@@ -190,16 +190,28 @@ __device__ __forceinline__ void store_block(uint16_t* __restrict__ C, const floa
 // c ^ ((r >> 1) & 7): the 8-byte writes (32 rows at one chunk) take the
 // minimum two LDS passes and the 16-byte reads are conflict-free.  A wave's
 // LDS accesses complete in order, so one round's reads finish before the
-// next round's writes reuse the strip.  Needs N % 8 == 0 and a 16-byte
-// aligned C; rows past M and pieces past N are skipped.
+// next round's writes reuse the strip.
+//  The stores are non-temporal buffer stores (cache policy nt): C is written
+//  once and never read here, and streaming it keeps the A and B panels in L2
+//  when every CU finishes a tile at the same moment (measured: +1.5% at
+//  8192^3 over plain stores).  Each round's descriptor covers the valid rows
+//  of its 32-row strip (at most 32 * 2^24 * 2 bytes), so rows past M fall
+//  outside it and the hardware drops them; pieces past N get an offset past
+//  every descriptor.  Needs N % 8 == 0 (a piece is wholly in or out) and a
+//  16-byte aligned C.
 template <int DT, int FN, int FM>
 __device__ __forceinline__ void store_tile_staged(uint16_t* __restrict__ C, const floatx16 (&acc)[FN][FM],
                                                   uint8_t* strip, int lane, int m_base, int n_base, int M, int N)
 {
     static_assert(FN % 2 == 0, "pairs of 32-column blocks");
+    constexpr int kNonTemporal = 2;   // cache policy nt
     const int rw = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FM; ++j) {
+        const int m_strip = m_base + 32 * j;
+        const int rows = max(0, min(32, M - m_strip));
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (size_t)max(0, min(m_strip, M)) * (size_t)N,
+                                                    (uint32_t)rows * (uint32_t)N * 2u);
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
 #pragma unroll
@@ -218,10 +230,12 @@ __device__ __forceinline__ void store_tile_staged(uint16_t* __restrict__ C, cons
             for (int s = 0; s < 4; ++s) {
                 const int r = 8 * s + (lane >> 3), c = lane & 7;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(strip + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-                const int m = m_base + 32 * j + r, n = n_base + 64 * p + 8 * c;
-                if (m < M && n < N) *reinterpret_cast<u32x4*>(C + (size_t)m * (size_t)N + n) = v;
+                const int n = n_base + 64 * p + 8 * c;
+                const uint32_t off = n < N ? ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u : kOobOffset;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, kNonTemporal);
             }
         }
+    }
 }
 
 // ---------------------------------------------------------------- tiled kernel
