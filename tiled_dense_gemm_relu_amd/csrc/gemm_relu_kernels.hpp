@@ -187,10 +187,12 @@ __device__ __forceinline__ void store_block(uint16_t* __restrict__ C, const floa
 // each row piece is read back and stored as 16-byte pieces, 8 lanes per
 // 128-byte row piece, instead of 8-byte pieces of 32 different rows.  Strip
 // rows are 128 bytes, and 16-byte chunk c of row r sits at chunk
-// c ^ ((r >> 1) & 7): the 8-byte writes (32 rows at one chunk) take the
-// minimum two LDS passes and the 16-byte reads are conflict-free.  A wave's
-// LDS accesses complete in order, so one round's reads finish before the
-// next round's writes reuse the strip.
+// c ^ ((r >> 1) & 7): the 16-byte reads (16 lanes: 2 rows x 8 chunks) are
+// conflict-free.  (The 8-byte writes show 4 bank-conflict cycles each in the
+// SQ counters with this layout, with its halves swapped in rows 16-31, and
+// as pairs of 4-byte writes spread over all 64 banks alike: measured, and
+// the same kernel time.)  A wave's LDS accesses complete in order, so one
+// round's reads finish before the next round's writes reuse the strip.
 //  The stores are non-temporal buffer stores (cache policy nt): C is written
 //  once and never read here, and streaming it keeps the A and B panels in L2
 //  when every CU finishes a tile at the same moment (measured: +1.5% at
