@@ -179,22 +179,27 @@ def gemm_relu_ex(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_AUTO
 
 
 _workspaces = {}
+_workspaces_lock = threading.Lock()
 
 
 def splitk_workspace(device, stream, nbytes: int):
     """A zero-filled workspace of at least ``nbytes`` for split-K calls on ``stream``.
 
-    One buffer per (device, stream), grown when needed and kept for later calls:
-    the library leaves its counters at zero after every completed call.  Calls
-    on one stream are ordered, so they may share it; other streams get their own.
+    One buffer per (device, stream), grown when needed and kept for later calls
+    until the process ends: the library leaves its counters at zero after every
+    completed call.  Calls on one stream are ordered, so they may share it;
+    other streams get their own.  A buffer that is replaced by a larger one is
+    released through torch's stream-ordered allocator, after the work already
+    queued on that stream.
     """
     import torch
     key = (device, stream.cuda_stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        with torch.cuda.stream(stream):
-            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    with _workspaces_lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            with torch.cuda.stream(stream):
+                ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
     return ws
 
 
