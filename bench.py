@@ -312,6 +312,12 @@ def main():
                      "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}
             entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
+            if not args.no_vendor and b_layout == binding.B_KN and s_config == binding.CONFIG_AUTO and s_splits is None:
+                # The same workload through torch.mm + torch.relu_ in this process, per step
+                # (launch gaps included on both sides): context, not a target.
+                v = time_vendor(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device)
+                entry["vendor_mm_relu_ms"] = v["mm_relu_ms"]
+                entry["fused_step_vs_mm_relu"] = round(v["mm_relu_ms"] / s_ms, 3)
             secondary[name] = entry
             log(f"[bench] {name}: {entry}")
 
