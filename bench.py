@@ -214,6 +214,24 @@ def cpu_baseline(w, target_s):
             "seconds": dt}
 
 
+def cpu_small(names=("small_256", "square_1024")):
+    """The CPU oracle on the small whole workloads, with one thread and with all host cores
+    (seconds of CPU in all): for scale beside the GPU's launch-bound small shapes."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    out = {}
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        a, b = inputs.workload_inputs(w)
+        entry = {}
+        for label, n in (("threads_1", 1), (f"threads_{threads}", threads)):
+            t = time.perf_counter()
+            oracle.gemm_relu(a, b, w.dtype, threads=n)
+            entry[label + "_ms"] = round((time.perf_counter() - t) * 1e3, 2)
+        out[name] = entry
+    return out
+
+
 def copy_calibration(device, n_bytes=1 << 30, reps=5):
     """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch give the
     factor between those counters and true HBM bytes."""
@@ -333,6 +351,8 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)
         log(f"[bench] CPU oracle: {cpu}")
         cpu.pop("seconds", None)
+        cpu["small_workloads"] = cpu_small()
+        log(f"[bench] CPU oracle, small whole workloads: {cpu['small_workloads']}")
 
     line = {
         "metric": METRIC,
