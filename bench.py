@@ -74,8 +74,8 @@ def make_sets(w, n_sets, device, b_layout=binding.B_KN):
 
 def sample_clocks(launch, seconds):
     """Keep the GPU busy with `launch` for about `seconds` while rocm-smi samples the shader
-    clock (and the package power where the board reports it).  Returns medians over the
-    samples after the first, or None if rocm-smi is unavailable."""
+    and memory clocks (and the package power where the board reports it).  Returns medians
+    over the samples after the first, or None if rocm-smi is unavailable."""
     samples, stop = [], threading.Event()
 
     def smi():
@@ -86,8 +86,10 @@ def sample_clocks(launch, seconds):
             except (OSError, subprocess.SubprocessError):
                 return
             clk = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
+            mclk = re.search(r"mclk clock level: \d+: \((\d+)Mhz\)", out)
             pwr = re.search(r"(?<!Max )Graphics Package Power \(W\): ([0-9.]+)", out)
-            samples.append((int(clk.group(1)) if clk else None, float(pwr.group(1)) if pwr else None))
+            samples.append((int(clk.group(1)) if clk else None, float(pwr.group(1)) if pwr else None,
+                            int(mclk.group(1)) if mclk else None))
 
     th = threading.Thread(target=smi, daemon=True)
     th.start()
@@ -99,11 +101,13 @@ def sample_clocks(launch, seconds):
         torch.cuda.synchronize()
     stop.set()
     th.join(timeout=15)
-    clks = sorted(c for c, _ in samples[1:] if c is not None)
-    pwrs = sorted(p for _, p in samples[1:] if p is not None)
+    clks = sorted(c for c, _, _ in samples[1:] if c is not None)
+    pwrs = sorted(p for _, p, _ in samples[1:] if p is not None)
+    mclks = sorted(m for _, _, m in samples[1:] if m is not None)
     if not clks:
         return None
     return {"sclk_mhz_median": clks[len(clks) // 2], "sclk_mhz_min": clks[0], "sclk_mhz_max": clks[-1],
+            "mclk_mhz_median": mclks[len(mclks) // 2] if mclks else None,
             "power_w_median": pwrs[len(pwrs) // 2] if pwrs else None, "samples": len(clks),
             "seconds": round(time.time() - t0, 2), "source": "rocm-smi --showclocks --showpower"}
 
