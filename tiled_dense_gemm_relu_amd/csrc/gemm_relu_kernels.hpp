@@ -933,6 +933,20 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     for (int u = 0; u < NF; ++u) read_unit(0, 0, 0, u);
     constexpr int NQC = WS ? 0 : NQ;   // DMAs a compute wave issues per step
 
+    // In the last k-step of a K-step, BAR_T MFMAs (on fragments already in
+    // registers) are issued before the barrier, so the matrix pipe stays busy
+    // while the waves meet; the next step's fragment reads follow the barrier.
+    // Measured at 8192^3 with 8 MFMAs per k-step: 1 / 2 / 3 / 4 before the
+    // barrier gave +0.8 / +1.4 / +0.7 / +0.3%.  Smaller wave tiles keep the
+    // barrier first.
+    constexpr int BAR_T = (!WS && NMF >= 8) ? 2 : 0;
+    static_assert(BAR_T < NMF && NKS >= 2, "the barrier is inside the last k-step, which issues no DMA");
+    auto step_barrier = [&]() {
+        __builtin_amdgcn_s_setprio(0);
+        if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
+        lds_barrier();                                   // ... and for every wave
+    };
+
     for (int g = 0; g < steps; ++g) {
         const int slot = g & (S - 1);
         const int slot_next = (g + 1) & (S - 1);
@@ -941,11 +955,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         for (int ks = 0; ks < NKS; ++ks) {
             const int cur = ks & 1, nxt = cur ^ 1;
             const bool last = ks == NKS - 1;
-            if (last) {
-                __builtin_amdgcn_s_setprio(0);
-                if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
-                lds_barrier();                // ... and for every wave
-            }
+            if (last && BAR_T == 0) step_barrier();
             // Issue priority 1 for the first k-steps of each K-step (MFMAs and
             // DMA issue), 0 from the barrier wait through the last k-step: of
             // the two waves sharing a SIMD, the one further along the K-step
@@ -957,12 +967,20 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             const int n_items = NF + (ks == 0 ? NQC : 0);
 #pragma unroll
             for (int t = 0; t < NMF; ++t) {
+                if (last && BAR_T > 0 && t == BAR_T) step_barrier();
                 // Snake order over the blocks: each MFMA changes one operand
                 // fragment from the one before (measured: about +0.4%).
                 const int bi = t / FM, bj = (bi & 1) ? FM - 1 - t % FM : t % FM;
                 acc[bi][bj] = mfma_32x32x16<DT>(fa[cur][bi], fb[cur][bj], acc[bi][bj]);
+                // This MFMA's share of the work items; in the last k-step they
+                // (reads of the next stage) start at the barrier.
+                const int t0 = last ? t - BAR_T : t, span = last ? NMF - BAR_T : NMF;
+                if (t0 < 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    continue;
+                }
 #pragma unroll
-                for (int u = t * n_items / NMF; u < (t + 1) * n_items / NMF; ++u) {
+                for (int u = t0 * n_items / span; u < (t0 + 1) * n_items / span; ++u) {
                     if (u < NF) {
                         if (last) read_unit(nxt, slot_next, 0, u);
                         else read_unit(nxt, slot, ks + 1, u);
