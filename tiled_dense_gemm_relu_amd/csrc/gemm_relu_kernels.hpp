@@ -941,6 +941,18 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // barrier first.
     constexpr int BAR_T = (!WS && NMF >= 8) ? 2 : 0;
     static_assert(BAR_T < NMF && NKS >= 2, "the barrier is inside the last k-step, which issues no DMA");
+    // Work items are numbered 0 .. NF-1 (fragment reads) and NF .. NF+NQC-1
+    // (DMAs).  In the first k-step the 256-wide wave tiles issue them
+    // alternately, a DMA first, so the DMAs start early without delaying the
+    // reads (measured at 8192^3: +1.6% over all reads first, +0.3% over all
+    // DMAs first).
+    constexpr bool ALTERNATE = !WS && NMF >= 8;
+    auto first_kstep_item = [](int u0) {
+        constexpr int PAIRS = NQC < NF ? NQC : NF;
+        if (!ALTERNATE) return u0;
+        if (u0 < 2 * PAIRS) return (u0 & 1) ? u0 / 2 : NF + u0 / 2;
+        return NQC > NF ? NF + (u0 - PAIRS) : u0 - PAIRS;
+    };
     auto step_barrier = [&]() {
         __builtin_amdgcn_s_setprio(0);
         if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
@@ -980,7 +992,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                     continue;
                 }
 #pragma unroll
-                for (int u = t0 * n_items / span; u < (t0 + 1) * n_items / span; ++u) {
+                for (int u0 = t0 * n_items / span; u0 < (t0 + 1) * n_items / span; ++u0) {
+                    const int u = ks == 0 ? first_kstep_item(u0) : u0;
                     if (u < NF) {
                         if (last) read_unit(nxt, slot_next, 0, u);
                         else read_unit(nxt, slot, ks + 1, u);
