@@ -937,8 +937,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // registers) are issued before the barrier, so the matrix pipe stays busy
     // while the waves meet; the next step's fragment reads follow the barrier.
     // Measured at 8192^3 with 8 MFMAs per k-step: 1 / 2 / 3 / 4 before the
-    // barrier gave +0.8 / +1.4 / +0.7 / +0.3%.  Smaller wave tiles keep the
-    // barrier first.
+    // barrier gave +0.8 / +1.4 / +0.7 / +0.3% (2: +0.7% on a second box).
+    // Smaller wave tiles keep the barrier first.
     constexpr int BAR_T = (!WS && NMF >= 8) ? 2 : 0;
     static_assert(BAR_T < NMF && NKS >= 2, "the barrier is inside the last k-step, which issues no DMA");
     // Work items are numbered 0 .. NF-1 (fragment reads) and NF .. NF+NQC-1
@@ -974,8 +974,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             // issues first (measured: about +1%).
             if (ks == 0) __builtin_amdgcn_s_setprio(1);
             // Work spread over this k-step's MFMAs: the next k-step's fragment
-            // reads (from the next stage after the barrier), then, in the first
-            // k-step, the DMAs of step g+S-1.
+            // reads (from the next stage after the barrier) and, in the first
+            // k-step, the DMAs of step g+S-1 (in the order first_kstep_item
+            // gives).
             const int n_items = NF + (ks == 0 ? NQC : 0);
 #pragma unroll
             for (int t = 0; t < NMF; ++t) {
