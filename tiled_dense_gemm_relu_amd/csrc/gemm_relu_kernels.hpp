@@ -942,11 +942,12 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     constexpr int BAR_T = (!WS && NMF >= 8) ? 2 : 0;
     static_assert(BAR_T < NMF && NKS >= 2, "the barrier is inside the last k-step, which issues no DMA");
     // Work items are numbered 0 .. NF-1 (fragment reads) and NF .. NF+NQC-1
-    // (DMAs).  In the first k-step the 256-wide wave tiles issue them
-    // alternately, a DMA first, so the DMAs start early without delaying the
-    // reads (measured at 8192^3: +1.6% over all reads first, +0.3% over all
-    // DMAs first).
-    constexpr bool ALTERNATE = !WS && NMF >= 8;
+    // (DMAs).  In the first k-step they are issued alternately, a DMA first,
+    // so the DMAs start early without delaying the reads.  Measured against
+    // all reads first: +1.6% at 8192^3 (256 tile; +0.3% over all DMAs
+    // first), +3.3% at 2048^3 (128 tile), +1.3% at 1024^3 and +0.8% on the
+    // 64 x 16384 x 8192 bf16 shape (64 tile).
+    constexpr bool ALTERNATE = !WS;
     auto first_kstep_item = [](int u0) {
         constexpr int PAIRS = NQC < NF ? NQC : NF;
         if (!ALTERNATE) return u0;
