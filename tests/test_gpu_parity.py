@@ -245,6 +245,31 @@ def test_nothing_written_outside_c(config):
     assert_within_tolerance(raw[guard:guard + M * N].reshape(M, N), oracle.gemm_relu(a, b, "fp16"), "fp16")
 
 
+def _random_staged_shapes(n=16, seed=2024):
+    # Seeded shapes with N % 8 == 0 (C in 16-byte row pieces, the staged
+    # epilogue) and ragged M and K: rows past M inside a 32-row strip, M below
+    # one strip, K tails of every residue mod 64.
+    import random
+    rng = random.Random(seed)
+    shapes = []
+    for _ in range(n):
+        M = rng.choice([rng.randint(1, 40), rng.randint(33, 700)])
+        N = 8 * rng.randint(1, 100)
+        K = rng.choice([rng.randint(1, 130), 8 * rng.randint(1, 64)])
+        shapes.append((M, N, K))
+    return shapes
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("shape", _random_staged_shapes())
+def test_random_shapes_staged_epilogue(shape, dtype):
+    M, N, K = shape
+    a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=M * 131 + N * 7 + K)
+    want = oracle.gemm_relu(a, b, dtype)
+    for config in (binding.CONFIG_AUTO, binding.CONFIG_DMA_256, binding.CONFIG_DMA_128, binding.CONFIG_DMA_256x128_WS):
+        assert np.array_equal(run_gpu(a, b, config), want), (shape, dtype, config)
+
+
 @pytest.mark.parametrize("c_off", [0, 4, 2, 1])
 @pytest.mark.parametrize("config", CONFIGS)
 def test_c_store_paths(c_off, config):
