@@ -22,6 +22,7 @@ import sys
 import threading
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ if ROOT not in sys.path:
 
 import tiled_dense_gemm_relu_amd as gr  # noqa: E402
 from tiled_dense_gemm_relu_amd import binding, inputs  # noqa: E402
+from tiled_dense_gemm_relu_amd.build import kernel_source_digest  # noqa: E402
 
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}     # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0                               # MI355X HBM3E, published
@@ -43,7 +45,6 @@ def measured_traffic(workload_name, kernel_name):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by the
     copy-kernel calibration; None unless they were taken on this workload, this kernel and the
     current kernel sources."""
-    from tiled_dense_gemm_relu_amd.build import kernel_source_digest
     try:
         with open(TRAFFIC_PROFILE) as f:
             prof = json.load(f)
@@ -205,7 +206,7 @@ def cpu_baseline(w, target_s):
     rows = max(1, threads)
     while True:
         t = time.perf_counter()
-        oracle.gemm_relu_rows(a, b, w.dtype, 0, rows, threads=threads)
+        ref_rows = oracle.gemm_relu_rows(a, b, w.dtype, 0, rows, threads=threads)
         dt = time.perf_counter() - t
         if dt >= 0.5 * target_s or rows >= w.M:
             break
@@ -215,7 +216,34 @@ def cpu_baseline(w, target_s):
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{rows_target - 1} of C ({rows_target} x {w.N} x {w.K}), "
                       f"{dt:.1f} s wall, fp64 accumulation",
-            "seconds": dt}
+            "seconds": dt}, ref_rows
+
+
+def parity_rows(w, ref_rows, device, b_layout):
+    """The GPU's C for the workload's seeded inputs (the oracle's), compared with the oracle's
+    rows from the CPU baseline: errors and the tolerance the tests use."""
+    a, b = inputs.workload_inputs(w)
+    if b_layout == binding.B_NK:
+        b = b.t().contiguous()
+    c = binding.gemm_relu_ex(a.to(device), b.to(device), b_layout=b_layout)
+    torch.cuda.synchronize(device)
+    rows = ref_rows.shape[0]
+    got_bits = c[:rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def values(bits):
+        if w.dtype == "fp16":
+            return bits.view(np.float16).astype(np.float64)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    g, r = values(got_bits), values(ref_rows)
+    err = np.abs(g - r)
+    tol = 1e-2 + 1e-2 * np.abs(r)
+    big = np.abs(r) >= 1e-2          # relative error where it means something
+    return {"rows_checked": int(rows), "elements": int(err.size), "max_abs_err": float(err.max()),
+            "max_rel_err_ref_ge_1e-2": float((err[big] / np.abs(r[big])).max()) if big.any() else 0.0,
+            "max_err_over_tolerance": round(float((err / tol).max()), 4),
+            "within_1e-2_tolerance": bool((err <= tol).all()),
+            "bit_identical_fraction": round(float((got_bits == ref_rows).mean()), 6)}
 
 
 def cpu_small(names=("small_256", "square_1024")):
@@ -317,14 +345,14 @@ def main():
                 ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None),
                 ("square_8192_bf16", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("square_8192", binding.B_KN, binding.CONFIG_DMA_256x128_WS, None)]
-        for name, b_layout, s_config, s_splits in runs:
+        for name, s_layout, s_config, s_splits in runs:
             sw = inputs.WORKLOADS[name]
             if (sw.name == w.name and s_splits is None and s_config == binding.CONFIG_AUTO and
-                    args.b_layout == ("nk" if b_layout == binding.B_NK else "kn")):
+                    args.b_layout == ("nk" if s_layout == binding.B_NK else "kn")):
                 continue
             s_ms, s_kms, _ = time_workload(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device, config=s_config,
-                                        b_layout=b_layout, splits=s_splits)
-            if b_layout == binding.B_NK:
+                                        b_layout=s_layout, splits=s_splits)
+            if s_layout == binding.B_NK:
                 name += "_b_nk"
             if s_splits is not None:
                 name += "_splitk" if s_config == binding.CONFIG_AUTO else f"_splitk{s_splits}_config{s_config}"
@@ -334,7 +362,7 @@ def main():
                      "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}
             entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
-            if not args.no_vendor and b_layout == binding.B_KN and s_config == binding.CONFIG_AUTO and s_splits is None:
+            if not args.no_vendor and s_layout == binding.B_KN and s_config == binding.CONFIG_AUTO and s_splits is None:
                 # The same workload through torch.mm + torch.relu_ in this process, per step
                 # (launch gaps included on both sides): context, not a target.
                 v = time_vendor(sw, 50 if sw.flop < 1e12 else 20, 10, 3, device)
@@ -349,12 +377,14 @@ def main():
         vendor["fused_kernel_vs_mm_relu"] = round(vendor["mm_relu_ms"] / ms_step, 3)
         log(f"[bench] vendor library (torch.mm, then torch.relu_): {vendor}")
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu, ref_rows = cpu_baseline(w, args.cpu_seconds)
         log(f"[bench] CPU oracle: {cpu}")
         cpu.pop("seconds", None)
+        parity = parity_rows(w, ref_rows, device, b_layout)
+        log(f"[bench] GPU against the oracle's rows: {parity}")
         cpu["small_workloads"] = cpu_small()
         log(f"[bench] CPU oracle, small whole workloads: {cpu['small_workloads']}")
 
@@ -381,6 +411,8 @@ def main():
                      "traffic": (measured_traffic(w.name, binding.CONFIG_NAMES.get(cfg["config_id"]))
                                  if b_layout == binding.B_KN else None)},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "kernel_source_sha256": kernel_source_digest(),
         "clocks": clocks,
         "vendor_reference": vendor,
         "secondary": secondary,
