@@ -358,7 +358,8 @@ def main():
                 name += "_splitk" if s_config == binding.CONFIG_AUTO else f"_splitk{s_splits}_config{s_config}"
             elif s_config != binding.CONFIG_AUTO:
                 name += "_" + binding.CONFIG_NAMES[s_config]
-            entry = {"ms": round(s_kms, 5), "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
+            entry = {"ms": round(s_kms, 5), "ms_per_step_batch": round(s_ms, 5),
+                     "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
                      "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}
             entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
