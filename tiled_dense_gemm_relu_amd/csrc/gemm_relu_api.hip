@@ -111,9 +111,9 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     plan->tile = -3;
     if (M == 0 || N == 0) return GEMM_RELU_OK;        // nothing to compute or write
 
-    const bool need_c = true;
+    // C is always written (K == 0 fills it with +0.0); A and B are read only when K > 0.
     const bool need_ab = K > 0;
-    if ((need_c && !C) || (need_ab && (!A || !B))) return GEMM_RELU_ERR_INVALID_ARG;
+    if (!C || (need_ab && (!A || !B))) return GEMM_RELU_ERR_INVALID_ARG;
     const uintptr_t odd = reinterpret_cast<uintptr_t>(C) | (need_ab ? (reinterpret_cast<uintptr_t>(A) |
                                                                       reinterpret_cast<uintptr_t>(B))
                                                                    : 0);
