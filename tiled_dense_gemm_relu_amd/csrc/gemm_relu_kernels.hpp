@@ -955,7 +955,6 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         return NQC > NF ? NF + (u0 - PAIRS) : u0 - PAIRS;
     };
     auto step_barrier = [&]() {
-        __builtin_amdgcn_s_setprio(0);
         if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
         lds_barrier();                                   // ... and for every wave
     };
@@ -969,11 +968,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             const int cur = ks & 1, nxt = cur ^ 1;
             const bool last = ks == NKS - 1;
             if (last && BAR_T == 0) step_barrier();
-            // Issue priority 1 for the first k-steps of each K-step (MFMAs and
-            // DMA issue), 0 from the barrier wait through the last k-step: of
-            // the two waves sharing a SIMD, the one further along the K-step
-            // issues first (measured: about +1%).
-            if (ks == 0) __builtin_amdgcn_s_setprio(1);
+            // (Raising the wave's issue priority for the first k-steps, s_setprio,
+            // once measured +1%; with the current schedule it costs 1% at
+            // 8192^3 and up to 2% on the smaller tiles, so it is not used.)
             // Work spread over this k-step's MFMAs: the next k-step's fragment
             // reads (from the next stage after the barrier) and, in the first
             // k-step, the DMAs of step g+S-1 (in the order first_kstep_item
@@ -1043,7 +1040,6 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             }
         }
     }
-    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
 }
 
