@@ -937,7 +937,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // registers) are issued before the barrier, so the matrix pipe stays busy
     // while the waves meet; the next step's fragment reads follow the barrier.
     // Measured at 8192^3 with 8 MFMAs per k-step: 1 / 2 / 3 / 4 before the
-    // barrier gave +0.8 / +1.4 / +0.7 / +0.3% (2: +0.7% on a second box).
+    // barrier gave +0.8 / +1.4 / +0.7 / +0.3% (2: +0.7% on a second machine).
     // Smaller wave tiles keep the barrier first.
     constexpr int BAR_T = (!WS && NMF >= 8) ? 2 : 0;
     static_assert(BAR_T < NMF && NKS >= 2, "the barrier is inside the last k-step, which issues no DMA");
