@@ -164,6 +164,29 @@ def test_square_8192_sampled(integer, name):
         assert 0.45 < (got == 0).mean() < 0.55
 
 
+@pytest.mark.parametrize("config", [binding.CONFIG_AUTO, binding.CONFIG_DMA_128])
+def test_c_larger_than_4_gib(config):
+    # C of 32800 x 65544 fp16 = 4.3 GB: element offsets past 2^31, and C stored
+    # through one buffer descriptor per 32-row strip.  Only sampled entries, the
+    # last rows and the last column come back to the host.
+    M, N, K = 32800, 65544, 16
+    a, b = inputs.integer_pair(M, N, K, torch.float16, seed=4242)
+    say(f"[C > 4 GiB, config {config}] GPU run")
+    c = gr.gemm_relu(a.cuda(), b.cuda(), config=config)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4242)
+    ii = np.concatenate([rng.integers(0, M, 4096), [M - 1] * 64, rng.integers(M - 40, M, 64)])
+    jj = np.concatenate([rng.integers(0, N, 4096), rng.integers(0, N, 64), [N - 1] * 64])
+    got = bits(c[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
+    assert np.array_equal(got, oracle.gemm_relu_entries(a, b, "fp16", ii, jj))
+    last_rows = bits(c[M - 2:])
+    assert np.array_equal(last_rows, oracle.gemm_relu_rows(a, b, "fp16", M - 2, M))
+    last_col = bits(c[:, N - 1])
+    assert np.array_equal(last_col, oracle.gemm_relu_entries(a, b, "fp16", np.arange(M), np.full(M, N - 1)))
+    del c
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("integer", [False, True])
 def test_skinny_64x16384x8192_bf16_full(integer):
     w = inputs.WORKLOADS["skinny_64x16384x8192"]
