@@ -164,6 +164,23 @@ def test_square_8192_sampled(integer, name):
         assert 0.45 < (got == 0).mean() < 0.55
 
 
+def test_k_of_a_million():
+    # K = 2^20 + 40 (a K tail), M and N tails: offsets along K up to 2 MiB per
+    # A row and B bands of 64 rows x N, through the plain and the split-K
+    # entry points.  Integer inputs: every fp32 partial sum is exact (< 2^24).
+    M, N, K = 264, 264, (1 << 20) + 40
+    a, b = inputs.integer_pair(M, N, K, torch.float16, seed=77)
+    rows = [0, 1, 127, 128, 255, 256, M - 1]
+    want = np.concatenate([oracle.gemm_relu_rows(a, b, "fp16", r, r + 1) for r in rows])
+    say("[K = 2^20 + 40] GPU runs")
+    ad, bd = a.cuda(), b.cuda()
+    c1 = gr.gemm_relu(ad, bd)
+    c2 = gr.gemm_relu_splitk(ad, bd, splits=0)
+    torch.cuda.synchronize()
+    for c in (c1, c2):
+        assert np.array_equal(bits(c)[rows], want)
+
+
 @pytest.mark.parametrize("config", [binding.CONFIG_AUTO, binding.CONFIG_DMA_128])
 def test_c_larger_than_4_gib(config):
     # C of 32800 x 65544 fp16 = 4.3 GB: element offsets past 2^31, and C stored
