@@ -104,8 +104,9 @@ enum {
     GEMM_RELU_CONFIG_DMA_256x128_WS = 7 /* 256x128x32 block tile, 4 direct-to-LDS stages, wave-
                                          specialised: 8 compute waves and 4 waves that only load */
     /* DMA_128, DMA_64, DMA_64x256 and DMA_256x128_WS need 16-byte loads of A and B (K % 8 == 0,
-       N % 8 == 0, 16-byte aligned A and B); DMA_256 also takes 4-byte loads (K and N even,
-       4-byte aligned A and B).  For other inputs a DMA_* request falls back to TILE_256
+       N % 8 == 0, 16-byte aligned A and B); DMA_256 also takes 4-byte aligned rows (K and N
+       even, 4-byte aligned A and B): 16-byte loads of A when B takes 16-byte loads (B stored
+       (K, N)), else 4-byte loads.  For other inputs a DMA_* request falls back to TILE_256
        (DMA_256, DMA_256x128_WS) or TILE_128 (DMA_128, DMA_64, DMA_64x256). */
 };
 

@@ -111,7 +111,8 @@ def test_config_choice_for_the_workload_shapes():
     assert (mid["config_id"], mid["block_m"], mid["grid"]) == (4, 128, 256)
     ragged = gr.selected_config(4000, 11000, 4100)
     assert ragged["config_id"] == 3 and ragged["grid"] == 16 * 43
-    assert (ragged["vec_a"], ragged["vec_b"]) == (2, 8)             # K % 8 == 4: 4-byte A DMA lanes
+    # K % 8 == 4: 16-byte A DMA lanes, BK = 64 in 2 stages; the piece straddling K is rewritten in LDS
+    assert (ragged["vec_a"], ragged["vec_b"], ragged["block_k"], ragged["stages"]) == (8, 8, 64, 2)
     odd = gr.selected_config(4000, 11000, 4101)
     assert (odd["config_id"], odd["vec_a"]) == (1, 1)               # odd K: register-staged kernel
     skinny = gr.selected_config(64, 16384, 8192, dtype=gr.BF16)
@@ -129,14 +130,20 @@ def test_load_width_follows_row_length_and_alignment(K, N, a_off, b_off, want):
 
 def test_dma_config_falls_back_without_suitable_loads():
     assert gr.selected_config(512, 512, 512, config=3)["config_id"] == 3
-    cfg = gr.selected_config(512, 512, 516, config=3)            # K % 8 != 0: 4-byte A lanes
-    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 8)
+    cfg = gr.selected_config(512, 512, 516, config=3)            # K % 8 != 0: still 16-byte A lanes
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"]) == (3, 8, 8, 64)
     cfg = gr.selected_config(512, 518, 512, config=3)            # N % 8 != 0: 4-byte B lanes
-    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 8, 2)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"]) == (3, 8, 2, 32)
+    cfg = gr.selected_config(512, 518, 516, config=3)            # ... and then 4-byte A lanes too
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
     cfg = gr.selected_config(512, 512, 515, config=3)            # odd K: register-staged kernel
     assert (cfg["config_id"], cfg["vec_a"]) == (1, 1)
-    cfg = gr.selected_config(512, 512, 512, config=3, a_ptr=4096 + 8)   # A only 8-byte aligned
-    assert (cfg["config_id"], cfg["vec_a"]) == (3, 2)
+    cfg = gr.selected_config(512, 512, 512, config=3, a_ptr=4096 + 8)   # A only 8-byte aligned: 16-byte lanes
+    assert (cfg["config_id"], cfg["vec_a"]) == (3, 8)
+    cfg = gr.selected_config(512, 512, 512, config=3, a_ptr=4096 + 4)   # ... or 4-byte aligned
+    assert (cfg["config_id"], cfg["vec_a"]) == (3, 8)
+    cfg = gr.selected_config(512, 512, 512, config=4, a_ptr=4096 + 8)   # other DMA tiles need 16-byte rows
+    assert cfg["config_id"] == 2
     assert gr.selected_config(512, 512, 512, config=3, a_ptr=4096 + 2)["config_id"] == 1
     for dma in (4, 5):
         assert gr.selected_config(512, 512, 512, config=dma)["config_id"] == dma

@@ -270,6 +270,41 @@ def test_odd_k(K):
             assert np.array_equal(run_gpu(a, b, config), want), (dtype, config)
 
 
+@pytest.mark.parametrize("a_off", [0, 2])
+@pytest.mark.parametrize("shape", [(300, 264, 2), (257, 520, 36), (64, 64, 6), (520, 776, 70),
+                                   (300, 264, 1030), (513, 1032, 764)])
+def test_k_straddling_piece(shape, a_off):
+    # K even but not a multiple of 8, B rows of 8-element multiples: the 256
+    # LDS-DMA kernel loads A with 16-byte lanes, so the last K-step's piece
+    # holding element K - 1 of a row also covers the first elements of the
+    # next row.  The kernel rewrites that piece with zeros past K.  +inf and
+    # NaN placed at the start of rows would otherwise reach the row above as
+    # inf * 0 = NaN.  A may also start 4 bytes into a buffer (rows 4-byte
+    # aligned only).
+    M, N, K = shape
+    for dtype in ("fp16", "bf16"):
+        a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=M + N + K)
+        a[1::3, 0] = float("inf")
+        a[2::5, 1] = float("nan")
+        b[0][b[0] == 0] = 1
+        want = oracle.gemm_relu(a, b, dtype)
+        assert np.isinf(values(want, dtype)).any()
+        abuf = torch.zeros(M * K + a_off, dtype=DT[dtype], device="cuda")
+        av = abuf[a_off:].view(M, K)
+        av.copy_(a)
+        for config in (binding.CONFIG_AUTO, binding.CONFIG_DMA_256):
+            cfg = gr.selected_config(M, N, K, dtype=gr.F16 if dtype == "fp16" else gr.BF16, config=config,
+                                     a_ptr=av.data_ptr(), b_ptr=1 << 20)
+            if config == binding.CONFIG_DMA_256:
+                assert (cfg["config_id"], cfg["vec_a"], cfg["block_k"]) == (3, 8, 64)
+            say(f"straddling piece: {shape} a_off={a_off} {dtype} config={config} -> {cfg['config_id']}")
+            c = gr.gemm_relu(av, b.cuda(), config=config)
+            torch.cuda.synchronize()
+            got = bits(c)
+            bad = np.argwhere(got != want)
+            assert bad.size == 0, (dtype, config, f"{len(bad)} differ, first at {tuple(bad[0])}")
+
+
 @pytest.mark.parametrize("config", CONFIGS)
 def test_nothing_written_outside_c(config):
     M, N, K = 250, 300, 70

@@ -23,6 +23,7 @@ struct Plan {
     int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 an LDS-DMA kernel (dma_id)
     int dma_id;        // DmaId when tile == -4
     int dma_a4, dma_b4;    // 4-byte DMA lanes for A / B (256 LDS-DMA kernel only)
+    int kfix;              // 256 LDS-DMA kernel, 16-byte A lanes, K even but not a multiple of 8
     int b_nk;          // B given as (N, K)
     int splits;        // K parts per tile (1: no split-K)
     int64_t counter_bytes;   // split-K workspace: per-tile counters, then the partial tiles
@@ -191,8 +192,12 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 
     if (chosen >= GEMM_RELU_CONFIG_DMA_256) {
         const int id = chosen - GEMM_RELU_CONFIG_DMA_256;
-        // 4-byte DMA lanes (256 tile only) use their own stage geometry.
-        const bool dword = id == kDma256 && (plan->b_nk ? !full_vectors : (va < 8 || vb < 8));
+        // 16-byte A lanes need only 4-byte aligned A rows in the 256 kernel
+        // when B stored (K, N) takes 16-byte lanes: where K % 8 != 0 its KTAIL 2
+        // instance rewrites the piece that straddles K.  4-byte DMA lanes (256
+        // tile only) use their own stage geometry.
+        const bool a16 = va == 8 || (id == kDma256 && !plan->b_nk && va >= 2 && vb == 8);
+        const bool dword = id == kDma256 && (plan->b_nk ? !full_vectors : (!a16 || vb < 8));
         const TileGeom& g = dword ? kDma256DwGeom : kDmaGeom[id];
         const int64_t b_band = plan->b_nk ? int64_t(g.bn) * K * 2 : int64_t(g.bk) * N * 2;
         if (int64_t(g.bm) * K * 2 > kMaxBand || b_band > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
@@ -207,9 +212,10 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         plan->cfg.block_k = g.bk;
         plan->cfg.stages = g.stages;
         plan->cfg.threads = g.threads;
-        plan->dma_a4 = va < 8 ? 1 : 0;     // only the 256 kernel gets here with va or vb < 8
+        plan->dma_a4 = a16 ? 0 : 1;        // only the 256 kernel gets here with va or vb < 8
         plan->dma_b4 = vb < 8 ? 1 : 0;
         if (plan->b_nk) plan->dma_a4 = plan->dma_b4 = full_vectors ? 0 : 1;   // one lane width for both
+        plan->kfix = !plan->b_nk && id == kDma256 && a16 && K % 8 != 0 ? 1 : 0;
         plan->cfg.vec_a = plan->dma_a4 ? 2 : 8;
         plan->cfg.vec_b = plan->dma_b4 ? 2 : 8;
         plan->cfg.grid = tm * tn;
@@ -328,7 +334,7 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
         const int ktail = K % p.cfg.block_k != 0 ? 1 : 0;
         const void* fn = p.splits > 1 ? ks.splitk[p.b_nk][p.dma_id][ktail]
                        : p.b_nk ? (p.dma_id == kDma256 && p.dma_a4 ? ks.dma256_nt_dw[ktail] : ks.dma_nt[p.dma_id][ktail])
-                       : p.dma_id == kDma256 ? ks.dma256_dw[p.dma_a4][p.dma_b4][ktail]
+                       : p.dma_id == kDma256 ? (p.kfix ? ks.dma256_kfix : ks.dma256_dw[p.dma_a4][p.dma_b4][ktail])
                                              : ks.dma[p.dma_id][ktail];
         // The LDS-DMA kernels are persistent: one workgroup per CU (their LDS
         // ring fills a CU), each walking every grid-th work unit.

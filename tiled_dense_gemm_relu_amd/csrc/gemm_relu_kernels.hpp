@@ -585,9 +585,16 @@ struct DmaConfig {
 
 // The LDS-DMA kernel: block tile BM x BN x BK, a ring of STAGES LDS stages
 // filled by direct-to-LDS loads, WAVES_M x WAVES_N waves of 32x32 MFMA blocks.
-// KTAIL: K is not a multiple of BK, so the last stage is partial and its A
-// pieces past K are masked (K must still be a multiple of the piece: 8
-// elements for 16-byte lanes, 2 for 4-byte lanes).
+// KTAIL 0: K is a multiple of BK.  KTAIL 1: it is not, so the last stage is
+// partial and its A pieces past K are masked (K must still be a multiple of
+// the piece: 8 elements for 16-byte lanes, 2 for 4-byte lanes).  KTAIL 2: as
+// 1, with 16-byte A lanes for any even K (rows 4-byte aligned).  When K % 8 is
+// not 0, the A piece holding element K - 1 also holds elements past K, which
+// its DMA takes from the next row (or reads as zero past the descriptor).
+// Once the last stage of a tile has landed, every thread rewrites half of one
+// row's such piece in LDS from two exact 4-byte loads (zero past K), and one
+// extra barrier orders those writes before the fragment reads.  KTAIL 2 needs
+// a 2-stage ring, B stored (K, N), no producer waves and two threads per row.
 // SPLITK: each tile's K range is cut into `splits` contiguous parts, each a
 // work unit of its own (for shapes with fewer tiles than CUs).  When a unit
 // finishes, each of its waves writes its fp32 partial sub-tile to `ws` and
@@ -596,7 +603,7 @@ struct DmaConfig {
 // not depend on which part finishes last), applies ReLU, stores C and resets
 // the counter to zero.  Nothing ever waits for another wave or workgroup.
 // Without SPLITK, `ws`, `counters` and `splits` are unused.
-template <class Cfg, int DT, bool KTAIL, bool SPLITK = false>
+template <class Cfg, int DT, int KTAIL, bool SPLITK = false>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok,
@@ -730,7 +737,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         const int k0 = f_kt * BK;
         if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
-            if (KTAIL) {   // pieces past K read as zero (K is a multiple of the piece length)
+            if (KTAIL) {   // pieces that start past K read as zero
                 vo = k0 + a_kcol[q] < K ? a_voff[q] + so : kOobOffset;
                 so = 0u;
             }
@@ -762,6 +769,35 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             f_b_ptr += (size_t)BK * (size_t)N;
         }
     };
+
+    // KTAIL 2: thread t owns dwords 2(t & 1) and 2(t & 1) + 1 of the last
+    // K-step's piece holding element K - 1 (logical chunk fx_chunk) in A row
+    // t / 2 of the tile.  fix_issue loads them when that stage is filled (rows
+    // past M and dwords past K read as zero); fix_apply writes them over what
+    // the DMA put there, once the stage has landed for every wave.
+    static_assert(KTAIL != 2 || (S == 2 && !WS && !Cfg::B_KMAJOR && LA == 16 && Cfg::THREADS == 2 * BM),
+                  "KTAIL 2 layout");
+    constexpr bool KFIX = KTAIL == 2;
+    const int fx_row = threadIdx.x >> 1;
+    const int fx_k = (KT - 1) * BK + 8 * (((K - 1) % BK) / 8) + 4 * (threadIdx.x & 1);   // first k of the two dwords
+    const uint32_t fx_lds = (uint32_t)(fx_row * A_ROW +
+                                       16 * ((((K - 1) % BK) / 8) ^ (Cfg::SWIZZLE ? a_swizzle<A_ROW>(fx_row) : 0)) +
+                                       8 * (threadIdx.x & 1));
+    u32x2 fx_val = {0u, 0u};
+    auto fix_issue = [&]() {
+        const int valid_m = min(BM, M - f_m0);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(A + (size_t)f_m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
+        const uint32_t off = (uint32_t)fx_row * (uint32_t)K * 2u + (uint32_t)fx_k * 2u;
+        fx_val.x = __builtin_amdgcn_raw_buffer_load_b32(rs, fx_k < K ? off : kOobOffset, 0, 0);
+        fx_val.y = __builtin_amdgcn_raw_buffer_load_b32(rs, fx_k + 2 < K ? off + 4u : kOobOffset, 0, 0);
+    };
+    auto fix_apply = [&](int slot) {
+        *reinterpret_cast<u32x2*>(smem + slot * Cfg::A_STAGE + fx_lds) = fx_val;
+        lds_barrier();
+    };
+    // Whether the stage the load side fills next is a tile's last K-step.
+    auto fill_is_last_kstep = [&]() { return KFIX && f_unit < n_units && f_kt == KT - 1; };
 
     // Per-lane LDS read offsets inside a stage.
     //  A fragment j, k-step ks: row wm*WTM + 32j + lane%32, chunk 2ks + lane/32.
@@ -901,9 +937,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     };
 
     // Prologue: steps 0 .. S-2 in flight, step 0 landed, its first k-step read.
+    bool fix_first = false;   // KTAIL 2 (S == 2): step 0 is a tile's last K-step
     if (!WS || producer) {
 #pragma unroll
         for (int s = 0; s < S - 1; ++s) {
+            if constexpr (KFIX) {
+                fix_first = fill_is_last_kstep();
+                if (fix_first) fix_issue();
+            }
 #pragma unroll
             for (int q = 0; q < NQ; ++q) dma(s, q);
             fill_advance();
@@ -911,6 +952,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         wait_vmcnt<(S - 2) * NQ>();
     }
     lds_barrier();
+    if constexpr (KFIX) {
+        if (fix_first) fix_apply(0);
+    }
     if constexpr (WS) {
         if (producer) {
             // The producer side of the ring: in step g, refill the slot step
@@ -954,15 +998,25 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         if (u0 < 2 * PAIRS) return (u0 & 1) ? u0 / 2 : NF + u0 / 2;
         return NQC > NF ? NF + (u0 - PAIRS) : u0 - PAIRS;
     };
-    auto step_barrier = [&]() {
-        if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
-        lds_barrier();                                   // ... and for every wave
-    };
-
     for (int g = 0; g < steps; ++g) {
         const int slot = g & (S - 1);
         const int slot_next = (g + 1) & (S - 1);
         const int slot_fill = (g + S - 1) & (S - 1);   // step g-1's slot: free since the last barrier
+        // KTAIL 2: the stage filled in this step (step g+1) is a tile's last
+        // K-step; its straddling pieces are loaded now and rewritten at the
+        // step barrier.
+        bool fix_now = false;
+        if constexpr (KFIX) {
+            fix_now = fill_is_last_kstep();
+            if (fix_now) fix_issue();
+        }
+        auto step_barrier = [&]() {
+            if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
+            lds_barrier();                                   // ... and for every wave
+            if constexpr (KFIX) {
+                if (fix_now) fix_apply(slot_next);
+            }
+        };
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int cur = ks & 1, nxt = cur ^ 1;

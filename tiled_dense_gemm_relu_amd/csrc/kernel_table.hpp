@@ -29,6 +29,10 @@ struct DtypeKernels {
     // The 256 LDS-DMA kernel with 4-byte DMA lanes: [A 4-byte][B 4-byte][K % BK != 0]
     // (index [0][0] unused: that is dma[kDma256]); need 2-element loads.
     const void* dma256_dw[2][2][2];
+    // The 256 LDS-DMA kernel with 16-byte lanes and K even but not a multiple
+    // of 8 (KTAIL 2: the piece straddling K is rewritten in LDS); needs
+    // 2-element loads of A and 8-element loads of B.
+    const void* dma256_kfix;
     // B given as B^T, an (N, K) row-major array: the direct kernel, the
     // LDS-DMA kernels with 16-byte lanes by DmaId and [K % BK != 0], and the
     // 256 one with 4-byte lanes by [K % BK != 0].

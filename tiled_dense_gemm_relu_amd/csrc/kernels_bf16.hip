@@ -75,6 +75,7 @@ DtypeKernels make_table()
     t.dma256_dw[0][1][1] = (const void*)&gemm_relu_dma<DmaTile256B4, kBF16, true>;
     t.dma256_dw[1][1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, kBF16, false>;
     t.dma256_dw[1][1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, kBF16, true>;
+    t.dma256_kfix = (const void*)&gemm_relu_dma<DmaTile256, kBF16, 2>;
     t.direct_nt = (const void*)&gemm_relu_direct<kBF16, true>;
     t.dma_nt[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256T, kBF16, false>;
     t.dma_nt[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256T, kBF16, true>;

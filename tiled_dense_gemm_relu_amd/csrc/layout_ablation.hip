@@ -46,7 +46,7 @@ float time_kernel(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int 
     float* ws = nullptr;
     int* counters = nullptr;
     void* args[] = {&A, &B, &C, &M, &N, &K, &tiles_m, &tiles_n, &c_vec_ok, &ws, &counters, &splits};
-    const void* fn = (const void*)&gemm_relu_dma<Cfg, kF16, false>;
+    const void* fn = (const void*)&gemm_relu_dma<Cfg, kF16, 0>;
     for (int i = 0; i < 3; ++i) CHECK(hipLaunchKernel(fn, dim3(grid), dim3(Cfg::THREADS), args, 0, nullptr));
     hipEvent_t t0, t1;
     CHECK(hipEventCreate(&t0));
