@@ -272,7 +272,10 @@ def test_odd_k(K):
 
 @pytest.mark.parametrize("a_off", [0, 2])
 @pytest.mark.parametrize("shape", [(300, 264, 2), (257, 520, 36), (64, 64, 6), (520, 776, 70),
-                                   (300, 264, 1030), (513, 1032, 764)])
+                                   (300, 264, 1030), (513, 1032, 764),
+                                   # more tiles than CUs: with one K-step per tile every step is a
+                                   # last K-step, so consecutive tiles each rewrite their piece
+                                   (4100, 4360, 6), (4100, 4360, 70)])
 def test_k_straddling_piece(shape, a_off):
     # K even but not a multiple of 8, B rows of 8-element multiples: the 256
     # LDS-DMA kernel loads A with 16-byte lanes, so the last K-step's piece
