@@ -308,6 +308,32 @@ def test_k_straddling_piece(shape, a_off):
             assert bad.size == 0, (dtype, config, f"{len(bad)} differ, first at {tuple(bad[0])}")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("config", CONFIGS)
+def test_subnormal_inputs(config, dtype):
+    # A holds only subnormals of its dtype: integers in {-2..2} times 2^-20 (fp16: below
+    # 2^-14) or 2^-130 (bf16: below 2^-126).  B holds integers times a power of two, so
+    # every product and partial sum is exact in fp32 and the oracle's exact result is
+    # what the GPU must give, bit for bit.  In fp16, sums of a few units come out as
+    # subnormals (below 2^-14) too.  A kernel that flushed subnormal inputs would give 0.
+    M, N, K = 256, 264, 136
+    ia, ib = inputs.integer_pair(M, N, K, torch.float32, seed=77)
+    a_scale, b_scale = (2.0 ** -20, 2.0 ** 4) if dtype == "fp16" else (2.0 ** -130, 2.0 ** 100)
+    a = (ia * a_scale).to(DT[dtype])
+    b = (ib * b_scale).to(DT[dtype])
+    av = a.to(torch.float64)
+    assert ((av == 0) | (av.abs() < (2.0 ** -14 if dtype == "fp16" else 2.0 ** -126))).all()
+    assert (av != 0).any() and torch.equal(av, ia.to(torch.float64) * a_scale)
+    want = oracle.gemm_relu(a, b, dtype)
+    wv = values(want, dtype)
+    assert (wv > 0).sum() > M * N // 4
+    if dtype == "fp16":
+        assert ((wv > 0) & (wv < 2.0 ** -14)).any()     # subnormal outputs are part of the check
+    got = run_gpu(a, b, config)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} differ, first at {tuple(bad[0])}"
+
+
 @pytest.mark.parametrize("config", CONFIGS)
 def test_nothing_written_outside_c(config):
     M, N, K = 250, 300, 70
