@@ -105,8 +105,9 @@ enum {
                                          specialised: 8 compute waves and 4 waves that only load */
     /* DMA_128, DMA_64, DMA_64x256 and DMA_256x128_WS need 16-byte loads of A and B (K % 8 == 0,
        N % 8 == 0, 16-byte aligned A and B); DMA_256 also takes 4-byte aligned rows (K and N
-       even, 4-byte aligned A and B): 16-byte loads of A when B takes 16-byte loads (B stored
-       (K, N)), else 4-byte loads.  For other inputs a DMA_* request falls back to TILE_256
+       even, 4-byte aligned A and B), with 16-byte loads, except that a B stored (K, N) whose
+       rows are not 16-byte multiples on 16-byte boundaries takes 4-byte loads, and A then
+       does too where K % 8 != 0.  For other inputs a DMA_* request falls back to TILE_256
        (DMA_256, DMA_256x128_WS) or TILE_128 (DMA_128, DMA_64, DMA_64x256). */
 };
 

@@ -169,11 +169,12 @@ def test_b_nk_config_choice():
     # B^T rows have length K: N no longer matters for the load width
     assert nt_config(1024, 1000, 1024)["config_id"] == 5
     assert nt_config(4000, 11003, 4096)["vec_b"] == 8
-    # K even but not a multiple of 8: the 256 kernel with 4-byte lanes for both operands
+    # K even but not a multiple of 8: the 256 kernel, 16-byte lanes for both operands, the
+    # pieces straddling K rewritten in LDS (BK = 64 in 2 stages)
     cfg = nt_config(1024, 1024, 1030)
-    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"], cfg["stages"]) == (3, 8, 8, 64, 2)
     cfg = nt_config(8192, 8192, 8192, b_ptr=(1 << 20) + 4)           # B^T only 4-byte aligned
-    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"]) == (3, 8, 8, 64)
     # odd K, or 2-byte alignment: the direct kernel
     assert nt_config(1024, 1024, 1031)["config_id"] == 0
     assert nt_config(8192, 8192, 8192, a_ptr=4096 + 2)["config_id"] == 0
@@ -189,7 +190,7 @@ def test_b_nk_forced_configs():
         assert nt_config(512, 512, 515, config=dma)["config_id"] == 0
     assert nt_config(512, 512, 515, config=0)["config_id"] == 0
     cfg = nt_config(512, 512, 516, config=1)
-    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 2, 2)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 8, 8)
 
 
 def test_splitk_config_choice():

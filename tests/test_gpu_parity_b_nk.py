@@ -104,6 +104,43 @@ def test_b_nk_unaligned_pointers(a_off, b_off, c_off, config):
     assert np.array_equal(bits(cv), want)
 
 
+@pytest.mark.parametrize("a_off,b_off", [(0, 0), (2, 2), (0, 2)])
+@pytest.mark.parametrize("shape", [(300, 264, 2), (257, 520, 36), (520, 776, 70), (513, 1032, 764),
+                                   (300, 270, 4098), (4100, 4360, 70)])
+def test_b_nk_k_straddling_pieces(shape, a_off, b_off):
+    # B^T rows hold K elements like A rows.  With K even but not a multiple of 8
+    # the 256 LDS-DMA kernel loads both with 16-byte lanes, and the last K-step's
+    # piece holding element K - 1 of a row also covers the start of the next row,
+    # in A and in B^T; past K, those two would multiply each other.  The kernel
+    # rewrites both pieces with zeros past K.  +inf and NaN at the start of rows
+    # of both operands must reach only the outputs whose sums contain them.
+    # A and B^T may start 4 bytes into a buffer (rows 4-byte aligned only).
+    M, N, K = shape
+    for dtype in ("fp16", "bf16"):
+        a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=M + N + K + 1)
+        a[1::3, 0] = float("inf")
+        a[2::5, 1] = float("nan")
+        b[0, 1::4] = float("inf")          # B^T rows 1, 5, 9, ... start with +inf
+        b[1, 3::7] = float("nan")
+        want = oracle.gemm_relu(a, b, dtype)
+        assert np.isinf(torch.from_numpy(want.view(np.int16)).view(DT[dtype]).float().numpy()).any()
+        abuf = torch.zeros(M * K + a_off, dtype=DT[dtype], device="cuda")
+        bbuf = torch.zeros(N * K + b_off, dtype=DT[dtype], device="cuda")
+        av, btv = abuf[a_off:].view(M, K), bbuf[b_off:].view(N, K)
+        av.copy_(a)
+        btv.copy_(b.t())
+        for config in (binding.CONFIG_AUTO, binding.CONFIG_DMA_256):
+            cfg = gr.selected_config(M, N, K, dtype=gr.F16 if dtype == "fp16" else gr.BF16, config=config,
+                                     a_ptr=av.data_ptr(), b_ptr=btv.data_ptr(), b_layout=gr.B_NK)
+            assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"]) == (3, 8, 8, 64)
+            say(f"B (N, K) straddling pieces: {shape} offsets {a_off},{b_off} {dtype} config={config}")
+            c = gr.gemm_relu_ex(av, btv, b_layout=gr.B_NK, config=config)
+            torch.cuda.synchronize()
+            got = bits(c)
+            bad = np.argwhere(got != want)
+            assert bad.size == 0, (dtype, config, f"{len(bad)} differ, first at {tuple(bad[0])}")
+
+
 @pytest.mark.parametrize("config", CONFIGS)
 def test_b_nk_nothing_written_outside_c(config):
     M, N, K = 250, 300, 72

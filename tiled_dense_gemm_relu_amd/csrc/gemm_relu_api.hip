@@ -22,8 +22,8 @@ struct Plan {
     gemm_relu_config_t cfg;
     int tile;          // TileId, -1 direct kernel, -2 K == 0 fill, -4 an LDS-DMA kernel (dma_id)
     int dma_id;        // DmaId when tile == -4
-    int dma_a4, dma_b4;    // 4-byte DMA lanes for A / B (256 LDS-DMA kernel only)
-    int kfix;              // 256 LDS-DMA kernel, 16-byte A lanes, K even but not a multiple of 8
+    int dma_a4, dma_b4;    // 4-byte DMA lanes for A / B (256 LDS-DMA kernel, B stored (K, N) only)
+    int kfix;              // 256 LDS-DMA kernel, 16-byte lanes, K even but not a multiple of 8 (KTAIL 2)
     int b_nk;          // B given as (N, K)
     int splits;        // K parts per tile (1: no split-K)
     int64_t counter_bytes;   // split-K workspace: per-tile counters, then the partial tiles
@@ -192,13 +192,17 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
 
     if (chosen >= GEMM_RELU_CONFIG_DMA_256) {
         const int id = chosen - GEMM_RELU_CONFIG_DMA_256;
-        // 16-byte A lanes need only 4-byte aligned A rows in the 256 kernel
-        // when B stored (K, N) takes 16-byte lanes: where K % 8 != 0 its KTAIL 2
-        // instance rewrites the piece that straddles K.  4-byte DMA lanes (256
-        // tile only) use their own stage geometry.
-        const bool a16 = va == 8 || (id == kDma256 && !plan->b_nk && va >= 2 && vb == 8);
-        const bool dword = id == kDma256 && (plan->b_nk ? !full_vectors : (!a16 || vb < 8));
-        const TileGeom& g = dword ? kDma256DwGeom : kDmaGeom[id];
+        // Lane widths.  The 256 kernel takes 16-byte lanes from any 4-byte
+        // aligned rows (the other DMA tiles are only chosen with 16-byte aligned
+        // rows of 8-element multiples).  Where K % 8 != 0, the K-contiguous row
+        // pieces that straddle K (A, and B^T when B is stored (N, K)) are
+        // rewritten in LDS by the KTAIL 2 instances, which need the 2-stage
+        // ring.  B stored (K, N) with rows not of 8-element multiples takes
+        // 4-byte lanes in a 4-stage ring of BK = 32, and then A does too where
+        // K % 8 != 0.
+        const bool b16 = plan->b_nk || vb == 8;
+        const bool a16 = b16 || K % 8 == 0;
+        const TileGeom& g = b16 ? kDmaGeom[id] : kDma256DwGeom;
         const int64_t b_band = plan->b_nk ? int64_t(g.bn) * K * 2 : int64_t(g.bk) * N * 2;
         if (int64_t(g.bm) * K * 2 > kMaxBand || b_band > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
         const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
@@ -213,11 +217,10 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         plan->cfg.stages = g.stages;
         plan->cfg.threads = g.threads;
         plan->dma_a4 = a16 ? 0 : 1;        // only the 256 kernel gets here with va or vb < 8
-        plan->dma_b4 = vb < 8 ? 1 : 0;
-        if (plan->b_nk) plan->dma_a4 = plan->dma_b4 = full_vectors ? 0 : 1;   // one lane width for both
-        plan->kfix = !plan->b_nk && id == kDma256 && a16 && K % 8 != 0 ? 1 : 0;
-        plan->cfg.vec_a = plan->dma_a4 ? 2 : 8;
-        plan->cfg.vec_b = plan->dma_b4 ? 2 : 8;
+        plan->dma_b4 = b16 ? 0 : 1;
+        plan->kfix = b16 && K % 8 != 0 ? 1 : 0;
+        plan->cfg.vec_a = a16 ? 8 : 2;
+        plan->cfg.vec_b = b16 ? 8 : 2;
         plan->cfg.grid = tm * tn;
         plan->cfg.lds_bytes = g.stages * (g.bm + g.bn) * g.bk * 2 + g.c_stage;
         if (splits_req >= 0 && has_splitk(id)) {
@@ -333,9 +336,9 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok, &ws, &counters, &splits};
         const int ktail = K % p.cfg.block_k != 0 ? 1 : 0;
         const void* fn = p.splits > 1 ? ks.splitk[p.b_nk][p.dma_id][ktail]
-                       : p.b_nk ? (p.dma_id == kDma256 && p.dma_a4 ? ks.dma256_nt_dw[ktail] : ks.dma_nt[p.dma_id][ktail])
-                       : p.dma_id == kDma256 ? (p.kfix ? ks.dma256_kfix : ks.dma256_dw[p.dma_a4][p.dma_b4][ktail])
-                                             : ks.dma[p.dma_id][ktail];
+                       : p.kfix ? (p.b_nk ? ks.dma_nt_kfix : ks.dma256_kfix)
+                       : p.dma_b4 ? ks.dma256_b4[p.dma_a4][ktail]
+                       : p.b_nk ? ks.dma_nt[p.dma_id][ktail] : ks.dma[p.dma_id][ktail];
         // The LDS-DMA kernels are persistent: one workgroup per CU (their LDS
         // ring fills a CU), each walking every grid-th work unit.
         const int64_t grid = std::min<int64_t>(p.cfg.grid, cus);

@@ -588,13 +588,14 @@ struct DmaConfig {
 // KTAIL 0: K is a multiple of BK.  KTAIL 1: it is not, so the last stage is
 // partial and its A pieces past K are masked (K must still be a multiple of
 // the piece: 8 elements for 16-byte lanes, 2 for 4-byte lanes).  KTAIL 2: as
-// 1, with 16-byte A lanes for any even K (rows 4-byte aligned).  When K % 8 is
-// not 0, the A piece holding element K - 1 also holds elements past K, which
-// its DMA takes from the next row (or reads as zero past the descriptor).
-// Once the last stage of a tile has landed, every thread rewrites half of one
-// row's such piece in LDS from two exact 4-byte loads (zero past K), and one
-// extra barrier orders those writes before the fragment reads.  KTAIL 2 needs
-// a 2-stage ring, B stored (K, N), no producer waves and two threads per row.
+// 1, with 16-byte lanes for K-contiguous rows (A, and B^T when B is stored
+// (N, K)) of any even K (rows 4-byte aligned).  When K % 8 is not 0, the piece
+// holding element K - 1 of such a row also holds elements past K, which its
+// DMA takes from the next row (or reads as zero past the descriptor).  Once
+// the last stage of a tile has landed, every thread rewrites half of one row's
+// such piece in LDS from two exact 4-byte loads (zero past K), for A and B^T,
+// and one extra barrier orders those writes before the fragment reads.
+// KTAIL 2 needs a 2-stage ring, no producer waves and two threads per row.
 // SPLITK: each tile's K range is cut into `splits` contiguous parts, each a
 // work unit of its own (for shapes with fewer tiles than CUs).  When a unit
 // finishes, each of its waves writes its fp32 partial sub-tile to `ws` and
@@ -771,11 +772,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     };
 
     // KTAIL 2: thread t owns dwords 2(t & 1) and 2(t & 1) + 1 of the last
-    // K-step's piece holding element K - 1 (logical chunk fx_chunk) in A row
-    // t / 2 of the tile.  fix_issue loads them when that stage is filled (rows
-    // past M and dwords past K read as zero); fix_apply writes them over what
-    // the DMA put there, once the stage has landed for every wave.
-    static_assert(KTAIL != 2 || (S == 2 && !WS && !Cfg::B_KMAJOR && LA == 16 && Cfg::THREADS == 2 * BM),
+    // K-step's piece holding element K - 1 in row t / 2 of the tile's A rows
+    // (and of its B^T rows when B is stored (N, K)).  fix_issue loads them when
+    // that stage is filled (rows past M or N and dwords past K read as zero);
+    // fix_apply writes them over what the DMA put there, once the stage has
+    // landed for every wave.  A and B^T rows have the same length and swizzle.
+    static_assert(KTAIL != 2 || (S == 2 && !WS && LA == 16 && Cfg::THREADS == 2 * BM &&
+                                 (!Cfg::B_KMAJOR || (LB == 16 && Cfg::THREADS == 2 * BN && B_ROW == A_ROW))),
                   "KTAIL 2 layout");
     constexpr bool KFIX = KTAIL == 2;
     const int fx_row = threadIdx.x >> 1;
@@ -783,17 +786,21 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     const uint32_t fx_lds = (uint32_t)(fx_row * A_ROW +
                                        16 * ((((K - 1) % BK) / 8) ^ (Cfg::SWIZZLE ? a_swizzle<A_ROW>(fx_row) : 0)) +
                                        8 * (threadIdx.x & 1));
-    u32x2 fx_val = {0u, 0u};
-    auto fix_issue = [&]() {
-        const int valid_m = min(BM, M - f_m0);
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(A + (size_t)f_m0 * (size_t)K, (uint32_t)valid_m * (uint32_t)K * 2u);
+    u32x2 fx_a = {0u, 0u}, fx_b = {0u, 0u};
+    auto fix_load = [&](const uint16_t* rows, int valid_rows) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(rows, (uint32_t)valid_rows * (uint32_t)K * 2u);
         const uint32_t off = (uint32_t)fx_row * (uint32_t)K * 2u + (uint32_t)fx_k * 2u;
-        fx_val.x = __builtin_amdgcn_raw_buffer_load_b32(rs, fx_k < K ? off : kOobOffset, 0, 0);
-        fx_val.y = __builtin_amdgcn_raw_buffer_load_b32(rs, fx_k + 2 < K ? off + 4u : kOobOffset, 0, 0);
+        return u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs, fx_k < K ? off : kOobOffset, 0, 0),
+                     __builtin_amdgcn_raw_buffer_load_b32(rs, fx_k + 2 < K ? off + 4u : kOobOffset, 0, 0)};
+    };
+    auto fix_issue = [&]() {
+        fx_a = fix_load(A + (size_t)f_m0 * (size_t)K, min(BM, M - f_m0));
+        if constexpr (Cfg::B_KMAJOR) fx_b = fix_load(B + (size_t)f_n0 * (size_t)K, min(BN, N - f_n0));
     };
     auto fix_apply = [&](int slot) {
-        *reinterpret_cast<u32x2*>(smem + slot * Cfg::A_STAGE + fx_lds) = fx_val;
+        *reinterpret_cast<u32x2*>(smem + slot * Cfg::A_STAGE + fx_lds) = fx_a;
+        if constexpr (Cfg::B_KMAJOR)
+            *reinterpret_cast<u32x2*>(smem + Cfg::B_REGION + slot * Cfg::B_STAGE + fx_lds) = fx_b;
         lds_barrier();
     };
     // Whether the stage the load side fills next is a tile's last K-step.
@@ -1103,17 +1110,16 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
 // A row piece a whole 128-byte line (one L2 request instead of two): +2.7% at
 // 8192^3, measured in one process.
 using DmaTile256 = DmaConfig<256, 256, 64, 2, 4, 2, 4>;
-// With 4-byte DMA lanes (rows of an even length), BK = 32 in 4 stages.
-using DmaTile256A4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 16>;   // ... A rows of an even length
-using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;   // ... B rows of an even length
-using DmaTile256AB4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4>;   // ... both
+// With 4-byte DMA lanes for B (K, N) rows of an even length but not a multiple
+// of 8, BK = 32 in 4 stages; A keeps 16-byte lanes where K % 8 == 0.
+using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;
+using DmaTile256AB4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4>;
 using DmaTile128 = DmaConfig<128, 128, 64, 4, 2, 2, 4>;   // mid shapes: 4 waves of 64x64
 using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny shapes: 4 waves of 32x32, 8 stages
 // few rows, many columns (with split-K): 4 waves of 64x64, 8 stages, 7 x 16 KiB of B in flight
 using DmaTile64x256 = DmaConfig<64, 256, 32, 8, 1, 4, 4>;
 // B given as B^T, (N, K) row-major
 using DmaTile256T = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, true>;
-using DmaTile256T4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4, true>;    // K even but not a multiple of 8
 using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
 using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
 using DmaTile64x256T = DmaConfig<64, 256, 32, 8, 1, 4, 4, 16, 16, true>;

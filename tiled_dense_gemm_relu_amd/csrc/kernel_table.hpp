@@ -26,19 +26,20 @@ struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
     const void* direct;
     const void* dma[5][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
-    // The 256 LDS-DMA kernel with 4-byte DMA lanes: [A 4-byte][B 4-byte][K % BK != 0]
-    // (index [0][0] unused: that is dma[kDma256]); need 2-element loads.
-    const void* dma256_dw[2][2][2];
-    // The 256 LDS-DMA kernel with 16-byte lanes and K even but not a multiple
-    // of 8 (KTAIL 2: the piece straddling K is rewritten in LDS); needs
-    // 2-element loads of A and 8-element loads of B.
+    // The 256 LDS-DMA kernel with 4-byte DMA lanes for B (B rows of an even
+    // length): [A 4-byte lanes][K % BK != 0].  A takes 16-byte lanes from any
+    // 4-byte aligned row where K % 8 == 0, else 4-byte lanes.
+    const void* dma256_b4[2][2];
+    // The 256 LDS-DMA kernel with 16-byte lanes from 4-byte aligned rows and K
+    // even but not a multiple of 8 (KTAIL 2: the piece straddling K is
+    // rewritten in LDS); for B stored (K, N) B needs 8-element loads.
     const void* dma256_kfix;
     // B given as B^T, an (N, K) row-major array: the direct kernel, the
     // LDS-DMA kernels with 16-byte lanes by DmaId and [K % BK != 0], and the
-    // 256 one with 4-byte lanes by [K % BK != 0].
+    // 256 one with KTAIL 2.
     const void* direct_nt;
     const void* dma_nt[5][2];
-    const void* dma256_nt_dw[2];
+    const void* dma_nt_kfix;
     // Split-K instances (8-element loads): [B layout][DmaId][K % BK != 0];
     // null for the 256 tiles, which have none.
     const void* splitk[2][5][2];
@@ -55,9 +56,9 @@ constexpr TileGeom kDmaGeom[kNumDma] = {
     {64, 256, 32, 8, 256, 4, 0},
     {256, 128, 32, 4, 768, 4, 32768},
 };
-// The 256 instances with 4-byte DMA lanes keep BK = 32 in 4 stages: with their
-// twice as many DMA instructions, the deeper ring measured faster (the ragged
-// 4000x11000x4100 shape: about 4%).
+// The 256 instances with 4-byte DMA lanes keep BK = 32 in 4 stages: with four
+// DMA instructions for every 16-byte one, the deeper ring measured about 4%
+// faster (on 4000x11000x4100 with 4-byte A lanes).
 constexpr TileGeom kDma256DwGeom = {256, 256, 32, 4, 512, 4, 32768};
 
 const DtypeKernels& kernels_f16();

@@ -24,8 +24,7 @@ constexpr bool dw_geom_matches = Cfg::BM == kDma256DwGeom.bm && Cfg::BN == kDma2
                                  Cfg::BK == kDma256DwGeom.bk && Cfg::STAGES == kDma256DwGeom.stages &&
                                  Cfg::THREADS == kDma256DwGeom.threads && Cfg::GROUP_M == kDma256DwGeom.group_m &&
                                  Cfg::C_STAGE_BYTES == kDma256DwGeom.c_stage;
-static_assert(dw_geom_matches<DmaTile256A4> && dw_geom_matches<DmaTile256B4> && dw_geom_matches<DmaTile256AB4> &&
-                  dw_geom_matches<DmaTile256T4>,
+static_assert(dw_geom_matches<DmaTile256B4> && dw_geom_matches<DmaTile256AB4>,
               "host geometry of the 4-byte-lane 256 instances out of date");
 static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
                   dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
@@ -67,14 +66,10 @@ DtypeKernels make_table()
     t.dma[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128, kF16, true>;
     t.dma[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64, kF16, false>;
     t.dma[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64, kF16, true>;
-    t.dma256_dw[0][0][0] = t.dma[kDma256][0];
-    t.dma256_dw[0][0][1] = t.dma[kDma256][1];
-    t.dma256_dw[1][0][0] = (const void*)&gemm_relu_dma<DmaTile256A4, kF16, false>;
-    t.dma256_dw[1][0][1] = (const void*)&gemm_relu_dma<DmaTile256A4, kF16, true>;
-    t.dma256_dw[0][1][0] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, false>;
-    t.dma256_dw[0][1][1] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, true>;
-    t.dma256_dw[1][1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, false>;
-    t.dma256_dw[1][1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, true>;
+    t.dma256_b4[0][0] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, 0>;
+    t.dma256_b4[0][1] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, 1>;
+    t.dma256_b4[1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, 0>;
+    t.dma256_b4[1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, 1>;
     t.dma256_kfix = (const void*)&gemm_relu_dma<DmaTile256, kF16, 2>;
     t.direct_nt = (const void*)&gemm_relu_direct<kF16, true>;
     t.dma_nt[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256T, kF16, false>;
@@ -83,8 +78,7 @@ DtypeKernels make_table()
     t.dma_nt[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128T, kF16, true>;
     t.dma_nt[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64T, kF16, false>;
     t.dma_nt[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64T, kF16, true>;
-    t.dma256_nt_dw[0] = (const void*)&gemm_relu_dma<DmaTile256T4, kF16, false>;
-    t.dma256_nt_dw[1] = (const void*)&gemm_relu_dma<DmaTile256T4, kF16, true>;
+    t.dma_nt_kfix = (const void*)&gemm_relu_dma<DmaTile256T, kF16, 2>;
     t.dma[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256, kF16, false>;
     t.dma[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256, kF16, true>;
     t.dma_nt[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256T, kF16, false>;
