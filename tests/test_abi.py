@@ -85,7 +85,7 @@ def test_unknown_b_layout_is_rejected(lib):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 8, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 9, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -157,6 +157,23 @@ def test_direct_config_geometry():
 
 def nt_config(M, N, K, **kw):
     return gr.selected_config(M, N, K, b_layout=gr.B_NK, **kw)
+
+
+def test_few_tiles_deep_k_takes_32x32_producer_tiles():
+    # 64x64 tiles would leave at least half the CUs idle: the plain entry point
+    # takes 32x32 tiles with producer waves (4 times as many tiles)
+    cfg = gr.selected_config(512, 512, 2048)
+    assert (cfg["config_id"], cfg["block_m"], cfg["block_n"], cfg["threads"], cfg["grid"]) == (8, 32, 32, 320, 256)
+    assert gr.selected_config(512, 512, 2048, b_layout=gr.B_NK)["config_id"] == 8
+    assert gr.selected_config(512, 520, 1024)["config_id"] == 8         # any K
+    assert gr.selected_config(1024, 1024, 4096)["config_id"] == 5       # 256 tiles of 64x64
+    # the split-K entry point keeps the 64x64 tile and splits K instead
+    sk = gr.selected_splitk_config(512, 512, 2048 + 64)
+    assert (sk["config_id"], sk["splits"] > 1) == (5, True)
+    # forced, it runs unsplit on either entry point; without 16-byte loads it falls back
+    assert gr.selected_splitk_config(512, 512, 4096, config=8)["splits"] == 1
+    assert gr.selected_config(512, 512, 2052, config=8)["config_id"] == 2
+    assert gr.selected_config(512, 512, 2052, config=8, b_layout=gr.B_NK)["config_id"] == 3
 
 
 def test_b_nk_config_choice():
@@ -247,7 +264,7 @@ def test_tuned_table_rows_are_what_auto_selects():
     assert len(rows) >= 10
     assert len({r[:5] for r in rows}) == len(rows)                       # one row per shape
     for M, N, K, dt, layout, config, sk_config, splits in rows:
-        assert 0 <= config <= 6 and 0 <= sk_config <= 6 and 1 <= splits <= 64
+        assert 0 <= config <= 8 and 0 <= sk_config <= 8 and 1 <= splits <= 64
         plain = gr.selected_config(M, N, K, dtype=dt, b_layout=layout)
         assert (plain["config_id"], plain["splits"]) == (config, 1), (M, N, K, layout)
         sk = gr.selected_splitk_config(M, N, K, dtype=dt, b_layout=layout)
@@ -255,10 +272,11 @@ def test_tuned_table_rows_are_what_auto_selects():
 
 
 def test_tuned_table_needs_the_tuners_alignment():
-    # The deep shape is tuned to split in 4; with B only 4-byte aligned the
-    # table does not apply and the heuristics choose (the register-staged 128 tile).
+    # The deep shape is tuned to split in 4 (and to 32x32 producer tiles without
+    # split-K); with B only 4-byte aligned the table does not apply and the
+    # heuristics choose (the register-staged 128 tile).
     rows = {r[:5]: r for r in tuned_table()}
-    assert rows[(512, 512, 16384, 0, 0)][5:] == (5, 5, 4)
+    assert rows[(512, 512, 16384, 0, 0)][5:] == (8, 5, 4)
     sk = gr.selected_splitk_config(512, 512, 16384, b_ptr=(1 << 20) + 4)
     assert (sk["config_id"], sk["splits"]) == (2, 1)
 

@@ -98,7 +98,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
     if (b_layout != GEMM_RELU_B_KN && b_layout != GEMM_RELU_B_NK) return GEMM_RELU_ERR_BAD_LAYOUT;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
-    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_256x128_WS)
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_32x32_WS)
         return GEMM_RELU_ERR_BAD_CONFIG;
     if (splits_req < -1 || splits_req > kMaxSplits) return GEMM_RELU_ERR_INVALID_ARG;
     if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
@@ -151,6 +151,13 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     // its K parts restore the parallelism the few tiles lack.
     if (chosen == GEMM_RELU_CONFIG_AUTO && splits_req >= 0 && full_vectors && M <= 64)
         chosen = GEMM_RELU_CONFIG_DMA_64x256;
+    // Few 64x64 tiles (at least half the CUs idle): the plain entry point,
+    // which has no workspace to split K with, takes 32x32 tiles with producer
+    // waves (4 times as many tiles; measured faster at 256^3, 512^3 and 512 x
+    // 512 x 16384).  The split-K entry point keeps the 64x64 tile and splits K
+    // instead (faster where it applies).
+    const bool few_tiles = splits_req < 0 && ceil_div(M, 64) * ceil_div(N, 64) < 128;
+    const int small_dma = few_tiles ? GEMM_RELU_CONFIG_DMA_32x32_WS : GEMM_RELU_CONFIG_DMA_64;
     if (plan->b_nk) {
         // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
         // operands, or 4-byte lanes for both in the 256 one) and the direct
@@ -161,12 +168,13 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
             if (t256 >= 192 || (!full_vectors && dword_vectors))
                 chosen = GEMM_RELU_CONFIG_DMA_256;
             else
-                chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_64;
+                chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : small_dma;
         }
         if (chosen == GEMM_RELU_CONFIG_TILE_256) chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_TILE_128) chosen = GEMM_RELU_CONFIG_DMA_128;
         if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
-             chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_256x128_WS) && !full_vectors)
+             chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_256x128_WS ||
+             chosen == GEMM_RELU_CONFIG_DMA_32x32_WS) && !full_vectors)
             chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_DIRECT;
     }
@@ -179,13 +187,13 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         if (t256 >= 192)
             chosen = dword_vectors ? GEMM_RELU_CONFIG_DMA_256 : GEMM_RELU_CONFIG_TILE_256;
         else if (full_vectors)
-            chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_64;
+            chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : small_dma;
         else
             chosen = GEMM_RELU_CONFIG_TILE_128;
     }
     if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
-         chosen == GEMM_RELU_CONFIG_DMA_64x256) && !full_vectors)
+         chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_32x32_WS) && !full_vectors)
         chosen = GEMM_RELU_CONFIG_TILE_128;
     if (chosen == GEMM_RELU_CONFIG_DMA_256x128_WS && !full_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     plan->cfg.config_id = chosen;

@@ -520,16 +520,19 @@ __device__ __forceinline__ int a_swizzle(int r)
         return (r ^ ((r >> 3) & 1)) & 7; // 2 rows share a 256-byte bank window
 }
 
-// Swizzle of the 16-byte chunks of one N-contiguous B row of ROW bytes (128,
-// 256 or 512).  A ds_read_b64_tr_b16 pair of 16-lane groups reads 4
+// Swizzle of the 16-byte chunks of one N-contiguous B row of ROW bytes (64,
+// 128, 256 or 512).  A ds_read_b64_tr_b16 pair of 16-lane groups reads 4
 // consecutive rows (k % 4 == 0) x 4 consecutive chunks (32 columns); the XOR
 // term spreads those 16 chunks over 16 distinct bank groups.  It depends on k
 // only through bits the fragment offsets (multiples of 4 rows) leave alone.
+// Rows of 64 bytes need none: 4 of them fill one 256-byte bank window.
 template <int ROW>
 __device__ __forceinline__ int b_swizzle(int k)
 {
-    static_assert(ROW == 128 || ROW == 256 || ROW == 512, "B rows of 64, 128 or 256 n");
-    if constexpr (ROW == 128)
+    static_assert(ROW == 64 || ROW == 128 || ROW == 256 || ROW == 512, "B rows of 32, 64, 128 or 256 n");
+    if constexpr (ROW == 64)
+        return 0;
+    else if constexpr (ROW == 128)
         return 4 * ((k >> 1) & 1);       // 2 rows share a 256-byte bank window
     else
         return 4 * (k & 3);              // every row starts at bank 0
@@ -1128,6 +1131,14 @@ using DmaTile64x256T = DmaConfig<64, 256, 32, 8, 1, 4, 4, 16, 16, true>;
 // producer wave beside its compute waves).
 using DmaTile256x128W = DmaConfig<256, 128, 32, 4, 4, 2, 4, 16, 16, false, 4>;
 using DmaTile256x128WT = DmaConfig<256, 128, 32, 4, 4, 2, 4, 16, 16, true, 4>;
+// Few output tiles and deep K: 32x32 tiles (4 times as many as 64x64 ones)
+// with one compute wave and 4 producer waves.  The producers keep the DMA
+// stream going while the compute wave works through its K-steps: on 512 x 512
+// x 16384 fp16, 42 us against 65 us for the 64x64x64 8-stage instance, in
+// one process (a single wave with no producers: 76 us; 8 stages instead of
+// 4: no faster, so bytes in flight are not the limit).
+using DmaTile32W = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, false, 4>;
+using DmaTile32WT = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, true, 4>;
 
 // ---------------------------------------------------------------- direct kernel
 

@@ -22,10 +22,13 @@ constexpr TileGeom kTileGeom[kNumTiles] = {
 constexpr int kNumVecPairs = 6;
 constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 2}, {1, 1}};
 
+// LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.
+enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kDma32W = 5, kNumDma = 6 };
+
 struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
     const void* direct;
-    const void* dma[5][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
+    const void* dma[kNumDma][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
     // The 256 LDS-DMA kernel with 4-byte DMA lanes for B (B rows of an even
     // length): [A 4-byte lanes][K % BK != 0].  A takes 16-byte lanes from any
     // 4-byte aligned row where K % 8 == 0, else 4-byte lanes.
@@ -38,23 +41,22 @@ struct DtypeKernels {
     // LDS-DMA kernels with 16-byte lanes by DmaId and [K % BK != 0], and the
     // 256 one with KTAIL 2.
     const void* direct_nt;
-    const void* dma_nt[5][2];
+    const void* dma_nt[kNumDma][2];
     const void* dma_nt_kfix;
     // Split-K instances (8-element loads): [B layout][DmaId][K % BK != 0];
     // null for the 256 tiles, which have none.
-    const void* splitk[2][5][2];
+    const void* splitk[2][kNumDma][2];
 };
 
-// LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.
-enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kNumDma = 5 };
 // Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64 / DmaTile64x256 /
-// DmaTile256x128W; threads include the producer waves).
+// DmaTile256x128W / DmaTile32W; threads include the producer waves).
 constexpr TileGeom kDmaGeom[kNumDma] = {
     {256, 256, 64, 2, 512, 4, 32768},
     {128, 128, 64, 4, 256, 4, 16384},
     {64, 64, 64, 8, 256, 4, 0},
     {64, 256, 32, 8, 256, 4, 0},
     {256, 128, 32, 4, 768, 4, 32768},
+    {32, 32, 64, 4, 320, 4, 0},
 };
 // The 256 instances with 4-byte DMA lanes keep BK = 32 in 4 stages: with four
 // DMA instructions for every 16-byte one, the deeper ring measured about 4%
