@@ -125,12 +125,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"gemm_relu: dtype must be float16 or bfloat16, got {t.dtype}")
 
 
-def _check_tensors(a, b, out, b_layout=B_KN):
+def _check_tensors(a, b, out, b_layout=B_KN) -> int:
+    """Argument checks of the tensor entry points; returns the device index."""
     import torch
     for name, t in (("a", a), ("b", b)) + ((("out", out),) if out is not None else ()):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"gemm_relu: {name} must be a torch.Tensor")
-        if t.device.type != "cuda":
+        if not t.is_cuda:
             raise ValueError(f"gemm_relu: {name} must be a GPU tensor, got {t.device}")
         if t.dim() != 2:
             raise ValueError(f"gemm_relu: {name} must be 2-D, got shape {tuple(t.shape)}")
@@ -142,10 +143,23 @@ def _check_tensors(a, b, out, b_layout=B_KN):
     if a.shape[1] != k_b:
         raise ValueError(f"gemm_relu: inner dimensions differ: a {tuple(a.shape)}, b {tuple(b.shape)}"
                          f" stored {'(N, K)' if b_layout == B_NK else '(K, N)'}")
-    if a.device != b.device or (out is not None and out.device != a.device):
+    dev = a.get_device()
+    if b.get_device() != dev or (out is not None and out.get_device() != dev):
         raise ValueError("gemm_relu: a, b and out must be on one device")
-    if out is not None and tuple(out.shape) != (a.shape[0], n):
+    if out is not None and (out.shape[0] != a.shape[0] or out.shape[1] != n):
         raise ValueError(f"gemm_relu: out must have shape {(a.shape[0], n)}, got {tuple(out.shape)}")
+    return dev
+
+
+def _stream_handle(stream, dev: int) -> int:
+    """The HIP stream handle to enqueue on: ``stream``'s, else the device's current one."""
+    import torch
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def gemm_relu(a, b, out=None, config: int = CONFIG_AUTO, stream=None):
@@ -166,16 +180,20 @@ def gemm_relu_ex(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_AUTO
     import torch
     if b_layout not in (B_KN, B_NK):
         raise ValueError(f"gemm_relu: b_layout must be B_KN or B_NK, got {b_layout}")
-    _check_tensors(a, b, out, b_layout)
+    dev = _check_tensors(a, b, out, b_layout)
     dtype = _dtype_code(a)
     M, K = a.shape
     N = b.shape[0] if b_layout == B_NK else b.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
-    s = stream if stream is not None else torch.cuda.current_stream(a.device)
-    with torch.cuda.device(a.device):
-        rc = gemm_relu_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, s.cuda_stream, config,
-                           b_layout)
+    handle = _stream_handle(stream, dev)
+    args = (a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, handle, config, b_layout)
+    # The library launches on the current device: make it the tensors' one.
+    if torch.cuda.current_device() == dev:
+        rc = gemm_relu_raw(*args)
+    else:
+        with torch.cuda.device(dev):
+            rc = gemm_relu_raw(*args)
     _check(rc)
     return out
 
