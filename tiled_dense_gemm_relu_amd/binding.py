@@ -65,6 +65,8 @@ def library_path() -> str:
 def load_library():
     """Load libgemm_relu.so (built in-tree by tiled_dense_gemm_relu_amd.build); raise if absent."""
     global _lib
+    if _lib is not None:          # loaded (the reference is only ever set once, under the lock)
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(_LIB_PATH):
