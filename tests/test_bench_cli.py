@@ -1,8 +1,12 @@
-"""bench.py's command-line contract, checked on the CPU: it measures one GPU
-only, and refuses to run without one rather than falling back."""
+"""bench.py's command-line contract: on the CPU, that it measures one GPU only
+and refuses to run without one rather than falling back; on a GPU, the fields
+of the JSON line it prints."""
+import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -23,3 +27,26 @@ def test_help_lists_the_contract_flags():
     assert res.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--workload", "--b-layout", "--clock-seconds", "--no-vendor"):
         assert flag in res.stdout
+
+
+@pytest.mark.gpu
+def test_bench_prints_the_contract_line():
+    # A short run on the 256^3 workload: one JSON line with the contract's fields;
+    # the timed region is K back-to-back launches, so the kernel's average launch
+    # duration over it gives roofline.achieved == value.
+    res = run("--workload", "small_256", "--steps", "5", "--warmup", "5", "--no-cpu-baseline", "--no-secondary",
+              "--no-vendor", "--clock-seconds", "0")
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [l for l in res.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    j = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in j, key
+    assert (j["n_gpus"], j["steps"], j["warmup"], j["unit"], j["dtype"], j["data"]) == (1, 5, 5, "TFLOP/s", "fp16",
+                                                                                        "synthetic")
+    assert j["config"]["workload"] == "small_256" and j["value"] > 0 and j["higher_is_better"] is True
+    r = j["roofline"]
+    assert (r["bound"], r["unit"], r["peak"]) == ("mfma", "TFLOP/s", 2500.0)
+    assert r["achieved"] == j["value"] and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    assert j["ms_per_launch_between_events"] > 0
