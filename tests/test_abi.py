@@ -85,7 +85,7 @@ def test_unknown_b_layout_is_rejected(lib):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 9, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 10, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -264,7 +264,7 @@ def test_tuned_table_rows_are_what_auto_selects():
     assert len(rows) >= 10
     assert len({r[:5] for r in rows}) == len(rows)                       # one row per shape
     for M, N, K, dt, layout, config, sk_config, splits in rows:
-        assert 0 <= config <= 8 and 0 <= sk_config <= 8 and 1 <= splits <= 64
+        assert 0 <= config <= 9 and 0 <= sk_config <= 9 and 1 <= splits <= 64
         plain = gr.selected_config(M, N, K, dtype=dt, b_layout=layout)
         assert (plain["config_id"], plain["splits"]) == (config, 1), (M, N, K, layout)
         sk = gr.selected_splitk_config(M, N, K, dtype=dt, b_layout=layout)

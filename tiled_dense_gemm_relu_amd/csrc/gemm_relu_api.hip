@@ -98,7 +98,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
     if (b_layout != GEMM_RELU_B_KN && b_layout != GEMM_RELU_B_NK) return GEMM_RELU_ERR_BAD_LAYOUT;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
-    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_32x32_WS)
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_64x64_WS)
         return GEMM_RELU_ERR_BAD_CONFIG;
     if (splits_req < -1 || splits_req > kMaxSplits) return GEMM_RELU_ERR_INVALID_ARG;
     if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
@@ -174,7 +174,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         if (chosen == GEMM_RELU_CONFIG_TILE_128) chosen = GEMM_RELU_CONFIG_DMA_128;
         if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
              chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_256x128_WS ||
-             chosen == GEMM_RELU_CONFIG_DMA_32x32_WS) && !full_vectors)
+             chosen == GEMM_RELU_CONFIG_DMA_32x32_WS || chosen == GEMM_RELU_CONFIG_DMA_64x64_WS) && !full_vectors)
             chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_DIRECT;
     }
@@ -193,7 +193,8 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     }
     if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
-         chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_32x32_WS) && !full_vectors)
+         chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_32x32_WS ||
+         chosen == GEMM_RELU_CONFIG_DMA_64x64_WS) && !full_vectors)
         chosen = GEMM_RELU_CONFIG_TILE_128;
     if (chosen == GEMM_RELU_CONFIG_DMA_256x128_WS && !full_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     plan->cfg.config_id = chosen;

@@ -1139,6 +1139,11 @@ using DmaTile256x128WT = DmaConfig<256, 128, 32, 4, 4, 2, 4, 16, 16, true, 4>;
 // 4: no faster, so bytes in flight are not the limit).
 using DmaTile32W = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, false, 4>;
 using DmaTile32WT = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, true, 4>;
+// The 64x64x64 tile with its 4 compute waves and 4 producer waves, 4 stages:
+// on 1024^3 fp16, 6.6-7.1 us against 7.8-8.3 us for DmaTile64 (8 stages, the
+// compute waves loading), in one process with bit-identical C.
+using DmaTile64W = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, false, 4>;
+using DmaTile64WT = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, true, 4>;
 
 // ---------------------------------------------------------------- direct kernel
 

@@ -23,7 +23,9 @@ constexpr int kNumVecPairs = 6;
 constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 2}, {1, 1}};
 
 // LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.
-enum DmaId { kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kDma32W = 5, kNumDma = 6 };
+enum DmaId {
+    kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kDma32W = 5, kDma64W = 6, kNumDma = 7
+};
 
 struct DtypeKernels {
     const void* tiled[kNumTiles][kNumVecPairs];
@@ -49,7 +51,7 @@ struct DtypeKernels {
 };
 
 // Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64 / DmaTile64x256 /
-// DmaTile256x128W / DmaTile32W; threads include the producer waves).
+// DmaTile256x128W / DmaTile32W / DmaTile64W; threads include the producer waves).
 constexpr TileGeom kDmaGeom[kNumDma] = {
     {256, 256, 64, 2, 512, 4, 32768},
     {128, 128, 64, 4, 256, 4, 16384},
@@ -57,6 +59,7 @@ constexpr TileGeom kDmaGeom[kNumDma] = {
     {64, 256, 32, 8, 256, 4, 0},
     {256, 128, 32, 4, 768, 4, 32768},
     {32, 32, 64, 4, 320, 4, 0},
+    {64, 64, 64, 4, 512, 4, 0},
 };
 // The 256 instances with 4-byte DMA lanes keep BK = 32 in 4 stages: with four
 // DMA instructions for every 16-byte one, the deeper ring measured about 4%

@@ -32,7 +32,8 @@ static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile1
                   dma_geom_matches<DmaTile64T, kDma64> && dma_geom_matches<DmaTile64x256, kDma64x256> &&
                   dma_geom_matches<DmaTile64x256T, kDma64x256> && dma_geom_matches<DmaTile256x128W, kDma256x128W> &&
                   dma_geom_matches<DmaTile256x128WT, kDma256x128W> && dma_geom_matches<DmaTile32W, kDma32W> &&
-                  dma_geom_matches<DmaTile32WT, kDma32W>,
+                  dma_geom_matches<DmaTile32WT, kDma32W> && dma_geom_matches<DmaTile64W, kDma64W> &&
+                  dma_geom_matches<DmaTile64WT, kDma64W>,
               "host DMA tile geometry out of date");
 
 template <class Cfg>
@@ -92,6 +93,10 @@ DtypeKernels make_table()
     t.dma[kDma32W][1] = (const void*)&gemm_relu_dma<DmaTile32W, kF16, 1>;
     t.dma_nt[kDma32W][0] = (const void*)&gemm_relu_dma<DmaTile32WT, kF16, 0>;
     t.dma_nt[kDma32W][1] = (const void*)&gemm_relu_dma<DmaTile32WT, kF16, 1>;
+    t.dma[kDma64W][0] = (const void*)&gemm_relu_dma<DmaTile64W, kF16, 0>;
+    t.dma[kDma64W][1] = (const void*)&gemm_relu_dma<DmaTile64W, kF16, 1>;
+    t.dma_nt[kDma64W][0] = (const void*)&gemm_relu_dma<DmaTile64WT, kF16, 0>;
+    t.dma_nt[kDma64W][1] = (const void*)&gemm_relu_dma<DmaTile64WT, kF16, 1>;
     fill_splitk<DmaTile128, DmaTile128T>(t, kDma128);
     fill_splitk<DmaTile64, DmaTile64T>(t, kDma64);
     fill_splitk<DmaTile64x256, DmaTile64x256T>(t, kDma64x256);
