@@ -106,7 +106,8 @@ def test_config_choice_for_the_workload_shapes():
     # the 128 KiB ring plus 8 waves x 4 KiB of C staging: the whole 160 KiB
     assert (big["stages"], big["vec_a"], big["vec_b"], big["grid"], big["lds_bytes"]) == (2, 8, 8, 1024, 163840)
     small = gr.selected_config(1024, 1024, 1024)
-    assert (small["config_id"], small["block_m"], small["stages"], small["grid"]) == (5, 64, 8, 256)
+    # 64x64x64 tiles with 4 producer waves in 4 stages (the tuned choice)
+    assert (small["config_id"], small["block_m"], small["stages"], small["threads"], small["grid"]) == (9, 64, 4, 512, 256)
     mid = gr.selected_config(2048, 2048, 2048)
     assert (mid["config_id"], mid["block_m"], mid["grid"]) == (4, 128, 256)
     ragged = gr.selected_config(4000, 11000, 4100)
@@ -116,7 +117,7 @@ def test_config_choice_for_the_workload_shapes():
     odd = gr.selected_config(4000, 11000, 4101)
     assert (odd["config_id"], odd["vec_a"]) == (1, 1)               # odd K: register-staged kernel
     skinny = gr.selected_config(64, 16384, 8192, dtype=gr.BF16)
-    assert (skinny["config_id"], skinny["grid"]) == (5, 256)
+    assert (skinny["config_id"], skinny["grid"]) == (9, 256)
 
 
 @pytest.mark.parametrize("K,N,a_off,b_off,want", [
@@ -166,7 +167,8 @@ def test_few_tiles_deep_k_takes_32x32_producer_tiles():
     assert (cfg["config_id"], cfg["block_m"], cfg["block_n"], cfg["threads"], cfg["grid"]) == (8, 32, 32, 320, 256)
     assert gr.selected_config(512, 512, 2048, b_layout=gr.B_NK)["config_id"] == 8
     assert gr.selected_config(512, 520, 1024)["config_id"] == 8         # any K
-    assert gr.selected_config(1024, 1024, 4096)["config_id"] == 5       # 256 tiles of 64x64
+    assert gr.selected_config(1024, 1024, 4096)["config_id"] == 9       # 256 tiles of 64x64, producer waves
+    assert gr.selected_splitk_config(1024, 1024, 4096)["config_id"] == 5     # split-K entry: no producers
     # the split-K entry point keeps the 64x64 tile and splits K instead
     sk = gr.selected_splitk_config(512, 512, 2048 + 64)
     assert (sk["config_id"], sk["splits"] > 1) == (5, True)
@@ -180,11 +182,11 @@ def test_b_nk_config_choice():
     big = nt_config(8192, 8192, 8192)
     assert (big["config_id"], big["vec_a"], big["vec_b"], big["b_layout"]) == (3, 8, 8, gr.B_NK)
     assert gr.selected_config(8192, 8192, 8192)["b_layout"] == gr.B_KN
-    assert nt_config(1024, 1024, 1024)["config_id"] == 5
+    assert nt_config(1024, 1024, 1024)["config_id"] == 9
     assert nt_config(2048, 2048, 2048)["config_id"] == 4
     assert nt_config(64, 16384, 8192, dtype=gr.BF16)["config_id"] == 5
     # B^T rows have length K: N no longer matters for the load width
-    assert nt_config(1024, 1000, 1024)["config_id"] == 5
+    assert nt_config(1024, 1000, 1024)["config_id"] == 9
     assert nt_config(4000, 11003, 4096)["vec_b"] == 8
     # K even but not a multiple of 8: the 256 kernel, 16-byte lanes for both operands, the
     # pieces straddling K rewritten in LDS (BK = 64 in 2 stages)

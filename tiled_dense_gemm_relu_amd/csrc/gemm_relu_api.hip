@@ -151,13 +151,16 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     // its K parts restore the parallelism the few tiles lack.
     if (chosen == GEMM_RELU_CONFIG_AUTO && splits_req >= 0 && full_vectors && M <= 64)
         chosen = GEMM_RELU_CONFIG_DMA_64x256;
-    // Few 64x64 tiles (at least half the CUs idle): the plain entry point,
-    // which has no workspace to split K with, takes 32x32 tiles with producer
-    // waves (4 times as many tiles; measured faster at 256^3, 512^3 and 512 x
-    // 512 x 16384).  The split-K entry point keeps the 64x64 tile and splits K
-    // instead (faster where it applies).
-    const bool few_tiles = splits_req < 0 && ceil_div(M, 64) * ceil_div(N, 64) < 128;
-    const int small_dma = few_tiles ? GEMM_RELU_CONFIG_DMA_32x32_WS : GEMM_RELU_CONFIG_DMA_64;
+    // The plain entry point's small tiles take producer waves: 64x64 tiles
+    // (measured faster at 1024^3), or, where 64x64 tiles would leave at least
+    // half the CUs idle, 32x32 ones (4 times as many tiles; measured faster at
+    // 256^3, 512^3 and 512 x 512 x 16384), since it has no workspace to split
+    // K with.  The split-K entry point keeps the 64x64 tile without producers,
+    // which has split-K instances, and splits K instead where it helps.
+    const bool few_tiles = ceil_div(M, 64) * ceil_div(N, 64) < 128;
+    const int small_dma = splits_req >= 0 ? GEMM_RELU_CONFIG_DMA_64
+                          : few_tiles     ? GEMM_RELU_CONFIG_DMA_32x32_WS
+                                          : GEMM_RELU_CONFIG_DMA_64x64_WS;
     if (plan->b_nk) {
         // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
         // operands, or 4-byte lanes for both in the 256 one) and the direct
