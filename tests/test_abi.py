@@ -168,7 +168,11 @@ def test_few_tiles_deep_k_takes_32x32_producer_tiles():
     assert gr.selected_config(512, 512, 2048, b_layout=gr.B_NK)["config_id"] == 8
     assert gr.selected_config(512, 520, 1024)["config_id"] == 8         # any K
     assert gr.selected_config(1024, 1024, 4096)["config_id"] == 9       # 256 tiles of 64x64, producer waves
-    assert gr.selected_splitk_config(1024, 1024, 4096)["config_id"] == 5     # split-K entry: no producers
+    # split-K entry: 256 tiles do not split, so the producer tiles too; asked for parts, the 64x64
+    # tile without producers (it has split-K instances)
+    assert (gr.selected_splitk_config(1024, 1024, 4096)["config_id"], gr.selected_splitk_config(1024, 1024, 4096)["splits"]) == (9, 1)
+    sk4 = gr.selected_splitk_config(1024, 1024, 4096, splits=4)
+    assert (sk4["config_id"], sk4["splits"]) == (5, 4)
     # the split-K entry point keeps the 64x64 tile and splits K instead
     sk = gr.selected_splitk_config(512, 512, 2048 + 64)
     assert (sk["config_id"], sk["splits"] > 1) == (5, True)

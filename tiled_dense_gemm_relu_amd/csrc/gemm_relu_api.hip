@@ -157,10 +157,13 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     // 256^3, 512^3 and 512 x 512 x 16384), since it has no workspace to split
     // K with.  The split-K entry point keeps the 64x64 tile without producers,
     // which has split-K instances, and splits K instead where it helps.
-    const bool few_tiles = ceil_div(M, 64) * ceil_div(N, 64) < 128;
-    const int small_dma = splits_req >= 0 ? GEMM_RELU_CONFIG_DMA_64
-                          : few_tiles     ? GEMM_RELU_CONFIG_DMA_32x32_WS
-                                          : GEMM_RELU_CONFIG_DMA_64x64_WS;
+    // (With the parts left to the library, the split-K entry point splits only
+    // below 192 tiles, so at or above that it takes the producer tiles too.)
+    const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64);
+    const bool few_tiles = t64 < 128;
+    const int small_dma = splits_req > 0 || (splits_req == 0 && t64 < 192) ? GEMM_RELU_CONFIG_DMA_64
+                          : few_tiles && splits_req < 0                   ? GEMM_RELU_CONFIG_DMA_32x32_WS
+                                                                          : GEMM_RELU_CONFIG_DMA_64x64_WS;
     if (plan->b_nk) {
         // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
         // operands, or 4-byte lanes for both in the 256 one) and the direct
