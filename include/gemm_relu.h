@@ -106,15 +106,17 @@ enum {
     GEMM_RELU_CONFIG_DMA_32x32_WS = 8, /* 32x32x64 block tile, 4 direct-to-LDS stages, one compute
                                          wave and 4 waves that only load (few output tiles, deep
                                          K: 4 times as many tiles as 64x64 ones, no workspace) */
-    GEMM_RELU_CONFIG_DMA_64x64_WS = 9 /* 64x64x64 block tile, 4 direct-to-LDS stages, 4 compute
+    GEMM_RELU_CONFIG_DMA_64x64_WS = 9, /* 64x64x64 block tile, 4 direct-to-LDS stages, 4 compute
                                          waves and 4 waves that only load */
-    /* DMA_128, DMA_64, DMA_64x256, DMA_256x128_WS, DMA_32x32_WS and DMA_64x64_WS need 16-byte loads of A and B
+    GEMM_RELU_CONFIG_DMA_128x128_WS = 10 /* 128x128x64 block tile, 4 direct-to-LDS stages, 4 compute
+                                         waves and 4 waves that only load */
+    /* DMA_128, DMA_64, DMA_64x256 and the *_WS configs need 16-byte loads of A and B
        (K % 8 == 0, N % 8 == 0, 16-byte aligned A and B); DMA_256 also takes 4-byte aligned rows (K and N
        even, 4-byte aligned A and B), with 16-byte loads, except that a B stored (K, N) whose
        rows are not 16-byte multiples on 16-byte boundaries takes 4-byte loads, and A then
        does too where K % 8 != 0.  For other inputs a DMA_* request falls back to TILE_256
        (DMA_256, DMA_256x128_WS) or TILE_128 (DMA_128, DMA_64, DMA_64x256, DMA_32x32_WS,
-       DMA_64x64_WS). */
+       DMA_64x64_WS, DMA_128x128_WS). */
 };
 
 /* What a configuration is, for reports and tests. */

@@ -85,7 +85,7 @@ def test_unknown_b_layout_is_rejected(lib):
 
 
 def test_unknown_config_is_rejected(lib):
-    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 10, None) == -8
+    assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, 11, None) == -8
     assert lib.gemm_relu_with_config(A_PTR, B_PTR, C_PTR, 4, 4, 4, 0, -2, None) == -8
 
 
@@ -187,7 +187,7 @@ def test_b_nk_config_choice():
     assert (big["config_id"], big["vec_a"], big["vec_b"], big["b_layout"]) == (3, 8, 8, gr.B_NK)
     assert gr.selected_config(8192, 8192, 8192)["b_layout"] == gr.B_KN
     assert nt_config(1024, 1024, 1024)["config_id"] == 9
-    assert nt_config(2048, 2048, 2048)["config_id"] == 4
+    assert nt_config(2048, 2048, 2048)["config_id"] == 10
     assert nt_config(64, 16384, 8192, dtype=gr.BF16)["config_id"] == 5
     # B^T rows have length K: N no longer matters for the load width
     assert nt_config(1024, 1000, 1024)["config_id"] == 9
@@ -270,7 +270,7 @@ def test_tuned_table_rows_are_what_auto_selects():
     assert len(rows) >= 10
     assert len({r[:5] for r in rows}) == len(rows)                       # one row per shape
     for M, N, K, dt, layout, config, sk_config, splits in rows:
-        assert 0 <= config <= 9 and 0 <= sk_config <= 9 and 1 <= splits <= 64
+        assert 0 <= config <= 10 and 0 <= sk_config <= 10 and 1 <= splits <= 64
         plain = gr.selected_config(M, N, K, dtype=dt, b_layout=layout)
         assert (plain["config_id"], plain["splits"]) == (config, 1), (M, N, K, layout)
         sk = gr.selected_splitk_config(M, N, K, dtype=dt, b_layout=layout)

@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 RTOL = ATOL = 1e-2
 CONFIGS = [binding.CONFIG_DIRECT, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128, binding.CONFIG_DMA_256,
            binding.CONFIG_DMA_128, binding.CONFIG_DMA_64, binding.CONFIG_DMA_64x256, binding.CONFIG_DMA_256x128_WS,
-           binding.CONFIG_DMA_32x32_WS, binding.CONFIG_DMA_64x64_WS]
+           binding.CONFIG_DMA_32x32_WS, binding.CONFIG_DMA_64x64_WS, binding.CONFIG_DMA_128x128_WS]
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 

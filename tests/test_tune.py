@@ -22,7 +22,7 @@ def test_default_shapes_cover_the_workloads_in_both_layouts():
 def test_candidates_are_distinct_resolved_configurations():
     cands = tune.candidates(512, 512, 16384, gr.F16, gr.B_KN)
     assert len(cands) == len(set(cands))
-    assert all(0 <= c <= 9 and 1 <= s <= 16 for c, s in cands)
+    assert all(0 <= c <= 10 and 1 <= s <= 16 for c, s in cands)
     assert (5, 4) in cands and (3, 1) in cands           # split-K on the 64 tile, the 256 tile
     assert (8, 1) in cands                               # 32x32 tiles with producer waves
     assert (0, 1) not in cands                           # the direct kernel only when nothing else runs

@@ -98,7 +98,7 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     if (dtype != GEMM_RELU_F16 && dtype != GEMM_RELU_BF16) return GEMM_RELU_ERR_BAD_DTYPE;
     if (b_layout != GEMM_RELU_B_KN && b_layout != GEMM_RELU_B_NK) return GEMM_RELU_ERR_BAD_LAYOUT;
     if (M < 0 || N < 0 || K < 0) return GEMM_RELU_ERR_INVALID_ARG;
-    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_64x64_WS)
+    if (config_id < GEMM_RELU_CONFIG_AUTO || config_id > GEMM_RELU_CONFIG_DMA_128x128_WS)
         return GEMM_RELU_ERR_BAD_CONFIG;
     if (splits_req < -1 || splits_req > kMaxSplits) return GEMM_RELU_ERR_INVALID_ARG;
     if (M > kMaxMN || N > kMaxMN || K > kMaxK) return GEMM_RELU_ERR_TOO_LARGE;
@@ -164,6 +164,9 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     const int small_dma = splits_req > 0 || (splits_req == 0 && t64 < 192) ? GEMM_RELU_CONFIG_DMA_64
                           : few_tiles && splits_req < 0                   ? GEMM_RELU_CONFIG_DMA_32x32_WS
                                                                           : GEMM_RELU_CONFIG_DMA_64x64_WS;
+    // 128x128 tiles run unsplit (192 or more of them) unless parts are asked
+    // for: with producer waves (measured faster at 2048^3).
+    const int mid_dma = splits_req > 0 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_128x128_WS;
     if (plan->b_nk) {
         // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
         // operands, or 4-byte lanes for both in the 256 one) and the direct
@@ -174,13 +177,14 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
             if (t256 >= 192 || (!full_vectors && dword_vectors))
                 chosen = GEMM_RELU_CONFIG_DMA_256;
             else
-                chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : small_dma;
+                chosen = t128 >= 192 ? mid_dma : small_dma;
         }
         if (chosen == GEMM_RELU_CONFIG_TILE_256) chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_TILE_128) chosen = GEMM_RELU_CONFIG_DMA_128;
         if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
              chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_256x128_WS ||
-             chosen == GEMM_RELU_CONFIG_DMA_32x32_WS || chosen == GEMM_RELU_CONFIG_DMA_64x64_WS) && !full_vectors)
+             chosen == GEMM_RELU_CONFIG_DMA_32x32_WS || chosen == GEMM_RELU_CONFIG_DMA_64x64_WS ||
+             chosen == GEMM_RELU_CONFIG_DMA_128x128_WS) && !full_vectors)
             chosen = GEMM_RELU_CONFIG_DMA_256;
         if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_DIRECT;
     }
@@ -193,14 +197,14 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         if (t256 >= 192)
             chosen = dword_vectors ? GEMM_RELU_CONFIG_DMA_256 : GEMM_RELU_CONFIG_TILE_256;
         else if (full_vectors)
-            chosen = t128 >= 192 ? GEMM_RELU_CONFIG_DMA_128 : small_dma;
+            chosen = t128 >= 192 ? mid_dma : small_dma;
         else
             chosen = GEMM_RELU_CONFIG_TILE_128;
     }
     if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
          chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_32x32_WS ||
-         chosen == GEMM_RELU_CONFIG_DMA_64x64_WS) && !full_vectors)
+         chosen == GEMM_RELU_CONFIG_DMA_64x64_WS || chosen == GEMM_RELU_CONFIG_DMA_128x128_WS) && !full_vectors)
         chosen = GEMM_RELU_CONFIG_TILE_128;
     if (chosen == GEMM_RELU_CONFIG_DMA_256x128_WS && !full_vectors) chosen = GEMM_RELU_CONFIG_TILE_256;
     plan->cfg.config_id = chosen;

@@ -1144,6 +1144,10 @@ using DmaTile32WT = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, true, 4>;
 // compute waves loading), in one process with bit-identical C.
 using DmaTile64W = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, false, 4>;
 using DmaTile64WT = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, true, 4>;
+// The same for the 128x128x64 tile: on 2048^3 fp16, 19.3-20.1 us against
+// 21.2-21.7 us for DmaTile128, in one process with bit-identical C.
+using DmaTile128W = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, false, 4>;
+using DmaTile128WT = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true, 4>;
 
 // ---------------------------------------------------------------- direct kernel
 

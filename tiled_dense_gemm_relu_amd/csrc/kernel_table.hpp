@@ -24,7 +24,8 @@ constexpr int kVecPairs[kNumVecPairs][2] = {{8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 
 
 // LDS-DMA kernel instances, by GEMM_RELU_CONFIG_DMA_* order.
 enum DmaId {
-    kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kDma32W = 5, kDma64W = 6, kNumDma = 7
+    kDma256 = 0, kDma128 = 1, kDma64 = 2, kDma64x256 = 3, kDma256x128W = 4, kDma32W = 5, kDma64W = 6, kDma128W = 7,
+    kNumDma = 8
 };
 
 struct DtypeKernels {
@@ -51,7 +52,7 @@ struct DtypeKernels {
 };
 
 // Geometry of each LDS-DMA instance (must match DmaTile256 / DmaTile128 / DmaTile64 / DmaTile64x256 /
-// DmaTile256x128W / DmaTile32W / DmaTile64W; threads include the producer waves).
+// DmaTile256x128W / DmaTile32W / DmaTile64W / DmaTile128W; threads include the producer waves).
 constexpr TileGeom kDmaGeom[kNumDma] = {
     {256, 256, 64, 2, 512, 4, 32768},
     {128, 128, 64, 4, 256, 4, 16384},
@@ -60,6 +61,7 @@ constexpr TileGeom kDmaGeom[kNumDma] = {
     {256, 128, 32, 4, 768, 4, 32768},
     {32, 32, 64, 4, 320, 4, 0},
     {64, 64, 64, 4, 512, 4, 0},
+    {128, 128, 64, 4, 512, 4, 16384},
 };
 // The 256 instances with 4-byte DMA lanes keep BK = 32 in 4 stages: with four
 // DMA instructions for every 16-byte one, the deeper ring measured about 4%

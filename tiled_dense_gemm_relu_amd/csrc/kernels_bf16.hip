@@ -33,7 +33,8 @@ static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile1
                   dma_geom_matches<DmaTile64x256T, kDma64x256> && dma_geom_matches<DmaTile256x128W, kDma256x128W> &&
                   dma_geom_matches<DmaTile256x128WT, kDma256x128W> && dma_geom_matches<DmaTile32W, kDma32W> &&
                   dma_geom_matches<DmaTile32WT, kDma32W> && dma_geom_matches<DmaTile64W, kDma64W> &&
-                  dma_geom_matches<DmaTile64WT, kDma64W>,
+                  dma_geom_matches<DmaTile64WT, kDma64W> && dma_geom_matches<DmaTile128W, kDma128W> &&
+                  dma_geom_matches<DmaTile128WT, kDma128W>,
               "host DMA tile geometry out of date");
 
 template <class Cfg>
@@ -97,6 +98,10 @@ DtypeKernels make_table()
     t.dma[kDma64W][1] = (const void*)&gemm_relu_dma<DmaTile64W, kBF16, 1>;
     t.dma_nt[kDma64W][0] = (const void*)&gemm_relu_dma<DmaTile64WT, kBF16, 0>;
     t.dma_nt[kDma64W][1] = (const void*)&gemm_relu_dma<DmaTile64WT, kBF16, 1>;
+    t.dma[kDma128W][0] = (const void*)&gemm_relu_dma<DmaTile128W, kBF16, 0>;
+    t.dma[kDma128W][1] = (const void*)&gemm_relu_dma<DmaTile128W, kBF16, 1>;
+    t.dma_nt[kDma128W][0] = (const void*)&gemm_relu_dma<DmaTile128WT, kBF16, 0>;
+    t.dma_nt[kDma128W][1] = (const void*)&gemm_relu_dma<DmaTile128WT, kBF16, 1>;
     fill_splitk<DmaTile128, DmaTile128T>(t, kDma128);
     fill_splitk<DmaTile64, DmaTile64T>(t, kDma64);
     fill_splitk<DmaTile64x256, DmaTile64x256T>(t, kDma64x256);

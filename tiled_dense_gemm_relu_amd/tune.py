@@ -62,7 +62,7 @@ def candidates(M, N, K, dt, layout):
     """Distinct (config_id, splits) pairs the library resolves requests to."""
     from . import binding
     seen = {}
-    for cfg in range(0, binding.CONFIG_DMA_64x64_WS + 1):
+    for cfg in range(0, binding.CONFIG_DMA_128x128_WS + 1):
         r = binding.selected_config(M, N, K, dt, cfg, b_layout=layout)
         if r["config_id"] == binding.CONFIG_DIRECT and cfg != binding.CONFIG_DIRECT:
             continue
