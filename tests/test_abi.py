@@ -109,7 +109,7 @@ def test_config_choice_for_the_workload_shapes():
     # 64x64x64 tiles with 4 producer waves in 4 stages (the tuned choice)
     assert (small["config_id"], small["block_m"], small["stages"], small["threads"], small["grid"]) == (9, 64, 4, 512, 256)
     mid = gr.selected_config(2048, 2048, 2048)
-    assert (mid["config_id"], mid["block_m"], mid["grid"]) == (4, 128, 256)
+    assert (mid["config_id"], mid["block_m"], mid["threads"], mid["grid"]) == (10, 128, 512, 256)   # producer waves
     ragged = gr.selected_config(4000, 11000, 4100)
     assert ragged["config_id"] == 3 and ragged["grid"] == 16 * 43
     # K % 8 == 4: 16-byte A DMA lanes, BK = 64 in 2 stages; the piece straddling K is rewritten in LDS
@@ -188,7 +188,7 @@ def test_b_nk_config_choice():
     assert gr.selected_config(8192, 8192, 8192)["b_layout"] == gr.B_KN
     assert nt_config(1024, 1024, 1024)["config_id"] == 9
     assert nt_config(2048, 2048, 2048)["config_id"] == 10
-    assert nt_config(64, 16384, 8192, dtype=gr.BF16)["config_id"] == 5
+    assert nt_config(64, 16384, 8192, dtype=gr.BF16)["config_id"] == 9
     # B^T rows have length K: N no longer matters for the load width
     assert nt_config(1024, 1000, 1024)["config_id"] == 9
     assert nt_config(4000, 11003, 4096)["vec_b"] == 8
