@@ -99,6 +99,53 @@ def test_encode_bf16_matches_torch_on_float32_values():
     assert np.array_equal(oracle.encode(x, "bf16"), bf16_bits_from_f32(x))
 
 
+def _bf16_nearest_by_search(x):
+    """Round doubles to bf16 bit patterns by search: the nearest entry of the table of every finite
+    bf16 value (decoded by torch), ties to the pattern with an even fraction, and past the largest
+    finite value by half its spacing or more to infinity.  It uses none of the oracle's arithmetic
+    (no binade, quantum or rint): only the value table and exact float64 comparisons.  The midpoint
+    of two neighbouring bf16 values has at most 9 significant bits, so it is an exact double and
+    x < mid, x == mid, x > mid decide the rounding exactly."""
+    pos_bits = np.arange(0, 0x7F80, dtype=np.uint16)            # +0 .. largest finite, increasing
+    vals = to_torch(pos_bits, torch.bfloat16).to(torch.float64).numpy()
+    top = 2.0 ** 128                                            # the next value past the largest
+    hi_vals = np.append(vals[1:], top)
+    hi_bits = np.append(pos_bits[1:], np.uint16(0x7F80))
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    i = np.searchsorted(vals, ax, side="right") - 1             # vals[i] <= ax < vals[i + 1]
+    lo, hi = vals[i], hi_vals[i]
+    mid = (lo + hi) / 2
+    up = (ax > mid) | ((ax == mid) & (pos_bits[i] & 1 == 1))
+    out = np.where(up, hi_bits[i], pos_bits[i]).astype(np.uint16)
+    out[ax >= top] = 0x7F80
+    return out | np.where(np.signbit(x), np.uint16(0x8000), np.uint16(0)).astype(np.uint16)
+
+
+def test_encode_bf16_of_any_double_is_a_single_rounding():
+    # Doubles with all 53 significant bits, and doubles within 2^-9 .. 2^-40 of a bf16 rounding
+    # midpoint on either side (bits far below float32's last place): rounding through float32 first
+    # would move many of them onto the midpoint.
+    x = _random_doubles(200_000, -140, 128, 21)
+    rng = np.random.default_rng(22)
+    v = rng.integers(0x0001, 0x7F7F, 20_000).astype(np.uint16)
+    vals = to_torch(v, torch.bfloat16).to(torch.float64).numpy()
+    nxt = to_torch(v + 1, torch.bfloat16).to(torch.float64).numpy()
+    mid = (vals + nxt) / 2
+    eps = np.ldexp(nxt - vals, -rng.integers(9, 40, v.size))
+    near = np.concatenate([mid, mid + eps, mid - eps])
+    x = np.concatenate([x, near, -near])
+    assert np.array_equal(oracle.encode(x, "bf16"), _bf16_nearest_by_search(x))
+
+
+def test_bf16_search_agrees_with_torch_on_float32_values():
+    # The search itself, against torch's float32 -> bf16 cast where that is a single rounding.
+    with np.errstate(over="ignore"):
+        x = _random_doubles(100_000, -140, 130, 23).astype(np.float32)
+    x = x[np.isfinite(x)].astype(np.float64)
+    assert np.array_equal(_bf16_nearest_by_search(x), bf16_bits_from_f32(x))
+
+
 def test_encode_bf16_ties_and_edges():
     # Worked by hand: bf16 keeps 8 significant bits.
     table = {
@@ -177,15 +224,15 @@ def test_integer_inputs_match_exact_integer_matmul_bf16(K):
 
 
 def _rne_via_library(x: Fraction, dtype):
-    """Round an exact rational with a library routine, when it is an exact double (else None)."""
+    """Round an exact rational when it is an exact double (else None): numpy's double -> fp16
+    cast, or for bf16 the search over torch's bf16 value table (any double, not only float32
+    values)."""
     d = float(x)
     if Fraction(d) != x:
         return None
     if dtype == "fp16":
         return int(f16_bits(d))
-    if Fraction(float(np.float32(d))) != x:
-        return None
-    return int(bf16_bits_from_f32(np.array([d]))[0])
+    return int(_bf16_nearest_by_search(np.array([d]))[0])
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -313,6 +360,9 @@ MUTANTS = {
     "truncating_cast": ("double n = rint(", "double n = trunc("),
     # ReLU applied to the wrong sign
     "keeps_negative_part": ("double r = s > 0.0 ? s : 0.0;", "double r = s < 0.0 ? -s : 0.0;"),
+    # double rounding: the fp64 sum rounded to float32 before the bf16 cast
+    "bf16_through_float32": ("uint16_t oracle_f64_to_bf16(double x) { return encode_rne(x,",
+                             "uint16_t oracle_f64_to_bf16(double x) { return encode_rne((double)(float)x,"),
 }
 
 
@@ -341,8 +391,9 @@ def _pins_pass(lib):
         M, K = ab.shape
         N = bb.shape[1]
         c = np.zeros((M, N), dtype=np.uint16)
+        dt = 1 if a.dtype == torch.bfloat16 else 0
         lib.oracle_gemm_relu(ab.ctypes.data_as(u16p), bb.ctypes.data_as(u16p), c.ctypes.data_as(u16p),
-                             M, N, K, 0, 0)
+                             M, N, K, dt, 0)
         return c
 
     a, b = inputs.integer_pair(9, 7, 33, torch.float16, seed=2)
@@ -351,10 +402,11 @@ def _pins_pass(lib):
         return False
     data = json.load(open(os.path.join(HERE, "golden", "hand_examples.json")))
     for ex in data["examples"]:
-        if ex["dtype"] != "fp16" or not ex["B"]:
+        if not ex["B"]:
             continue
+        tdt = torch.float16 if ex["dtype"] == "fp16" else torch.bfloat16
         A, B = np.array(ex["A"], dtype=np.float64), np.array(ex["B"], dtype=np.float64)
-        got = run(torch.from_numpy(A).to(torch.float16), torch.from_numpy(B).to(torch.float16))
+        got = run(torch.from_numpy(A).to(tdt), torch.from_numpy(B).to(tdt))
         want = np.array([[int(h, 16) for h in row] for row in ex["C_bits"]], dtype=np.uint16)
         if not np.array_equal(got, want):
             return False
