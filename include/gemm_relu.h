@@ -153,9 +153,27 @@ int gemm_relu_with_config(const void* A, const void* B, void* C, int64_t M, int6
 
 /* The configuration gemm_relu would use for these arguments (pure host logic:
  * no device is touched).  `out` may be NULL.  Returns GEMM_RELU_OK or the
- * error gemm_relu would return for these arguments' shape, dtype or alignment. */
+ * error gemm_relu would return for these arguments' shape, dtype or alignment.
+ * The GEMM page's kernel factory takes the block sizes (block_M, block_N,
+ * block_K) and the pipeline's stage count as explicit parameters ("Writing
+ * High-Performance Kernels in TileLang", atlascloud.ai, section "Let's write a
+ * GEMM"); here the library picks them per shape, and this call reports the
+ * pick with everything else that depends on the pointers (load widths, grid). */
 int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t M, int64_t N,
                            int64_t K, int dtype, int config_id, gemm_relu_config_t* out);
+
+/* The block tile and stage count gemm_relu picks for an (M, N, K) problem of
+ * `dtype`, for dense row-major A, B and C on 256-byte aligned, separate
+ * allocations (what a device allocator returns): the block_M, block_N, block_K
+ * and num_stages that the GEMM page's kernel factory takes as parameters
+ * ("Writing High-Performance Kernels in TileLang", atlascloud.ai, section
+ * "Let's write a GEMM").  block_k and stages are 0 for the direct kernel; for
+ * K == 0 (a fill of +0.0) all four are 0.  Any output pointer may be NULL.
+ * Pure host logic: no device is touched.  Returns GEMM_RELU_OK, or the error
+ * gemm_relu would return for this shape and dtype (then the outputs are not
+ * written).  gemm_relu_query_config gives the full record for given pointers. */
+int gemm_relu_selected_config(int64_t M, int64_t N, int64_t K, int dtype, int* bm, int* bn, int* bk,
+                              int* stages);
 
 /*
  * C = ReLU(A @ B) with B stored as `b_layout` says (GEMM_RELU_B_*) and a kernel
@@ -193,13 +211,15 @@ int gemm_relu_query_config_ex(const void* A, const void* B, const void* C, int64
  * run to run; on integer-valued inputs they equal gemm_relu's bit for bit, on
  * real-valued inputs they differ from it only by fp32 summation order.
  *
- * splits: 0 lets the library choose (enough parts for about 256 work units
- * when the tiles alone are fewer than 192, else 1); n >= 1 asks for n parts.
- * Either is capped at the tile's number of K-steps and at 64.  Only the
- * DMA_128, DMA_64 and DMA_64x256 kernels split; with other configurations, or
- * when the count resolves to 1, the call is gemm_relu_ex (workspace unused, may
- * be NULL).  With GEMM_RELU_CONFIG_AUTO and M <= 64 the DMA_64x256 tile is
- * chosen when its loads are possible.
+ * splits: 0 lets the library choose (with GEMM_RELU_CONFIG_AUTO, a shape in
+ * the tuned table takes the table's tile and parts; otherwise enough parts for
+ * about 256 work units when the tiles alone are fewer than 192, else 1);
+ * n >= 1 asks for n parts.  Either is capped at the tile's number of K-steps
+ * and at 64.  Only the DMA_128, DMA_64 and DMA_64x256 kernels split; with other
+ * configurations, or when the count resolves to 1, the call is gemm_relu_ex
+ * (workspace unused, may be NULL).  With GEMM_RELU_CONFIG_AUTO and n >= 1 the
+ * tile is always one that splits: the tuned table's, if it splits, else by the
+ * size rules, which take DMA_64x256 for M <= 64 when its loads are possible.
  *
  * workspace: device memory of at least gemm_relu_config_t.workspace_bytes
  * (from gemm_relu_query_splitk with the same arguments), 256-byte aligned,
@@ -222,7 +242,13 @@ int gemm_relu_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N
 int gemm_relu_query_splitk(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
                            int dtype, int b_layout, int config_id, int splits, gemm_relu_config_t* out);
 
-/* A static, human-readable description of a return code. */
+/* A static, human-readable description of a return code.  The pages' GEMM
+ * surfaces its failures at two points, when the kernel is built (layout and
+ * fragment-shape errors) and when it runs (out-of-bounds accesses from a wrong
+ * grid or K loop, shared memory over budget at launch) (zwxr.cn hands-on
+ * TileLang article, sections 5.1 and 5.2).  This library has no build step at
+ * call time: every such condition is checked on the host before anything is
+ * launched and returned as one of the codes above, which this call names. */
 const char* gemm_relu_strerror(int code);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

@@ -31,7 +31,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gemm_relu", "gemm_relu_with_config", "gemm_relu_query_config", "gemm_relu_strerror",
         "gemm_relu_version", "gemm_relu_ex", "gemm_relu_query_config_ex", "gemm_relu_splitk",
-        "gemm_relu_query_splitk"])
+        "gemm_relu_query_splitk", "gemm_relu_selected_config"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -297,3 +297,48 @@ def test_wave_specialised_config():
     assert gr.selected_config(512, 512, 516, config=7, b_layout=gr.B_NK)["config_id"] == 3
     # never split
     assert gr.selected_splitk_config(512, 512, 4096, config=7, splits=4)["splits"] == 1
+
+
+@pytest.mark.parametrize("shape", [
+    (256, 256, 256, 0), (1024, 1024, 1024, 0), (2048, 2048, 2048, 0), (8192, 8192, 8192, 0),
+    (4000, 11000, 4100, 0), (64, 16384, 8192, 1), (512, 512, 16384, 0), (8192, 8192, 8192, 1),
+    (100, 70, 9, 0), (4000, 11000, 4101, 0), (512, 518, 516, 0), (3, 5, 0, 0), (1, 1, 1, 1)])
+def test_selected_config_agrees_with_the_full_query(lib, shape):
+    # gemm_relu_selected_config (the block sizes and stage count the pages' kernel factory takes)
+    # reports what gemm_relu_query_config gives for separate, 256-byte aligned buffers.
+    M, N, K, dt = shape
+    base = 1 << 32
+    a, b, c = base, base + (1 << 36), base + (2 << 36)
+    q = gr.selected_config(M, N, K, dtype=dt, a_ptr=a, b_ptr=b, c_ptr=c)
+    assert gr.selected_block_config(M, N, K, dt) == (q["block_m"], q["block_n"], q["block_k"], q["stages"])
+
+
+def test_selected_config_values_and_errors(lib):
+    assert gr.selected_block_config(8192, 8192, 8192) == (256, 256, 64, 2)
+    assert gr.selected_block_config(1024, 1024, 1024) == (64, 64, 64, 4)
+    out = [ctypes.c_int(-7) for _ in range(4)]
+    refs = [ctypes.byref(v) for v in out]
+    assert lib.gemm_relu_selected_config(4, 4, 4, 5, *refs) == -2              # bad dtype
+    assert lib.gemm_relu_selected_config(-1, 4, 4, 0, *refs) == -1             # negative M
+    assert lib.gemm_relu_selected_config(4, 4, (1 << 22) + 1, 0, *refs) == -7  # too large
+    assert [v.value for v in out] == [-7] * 4                                  # untouched on error
+    assert lib.gemm_relu_selected_config(64, 64, 64, 0, None, None, None, None) == 0
+
+
+def test_explicit_parts_are_never_dropped_by_the_tuned_table():
+    # 2048^3 is tuned to the 128x128 producer-wave tile, which has no split-K kernels: asked for
+    # 4 parts, AUTO takes the 128x128 tile that splits, as for an untuned shape of that size.
+    sk = gr.selected_splitk_config(2048, 2048, 2048, splits=4)
+    assert (sk["config_id"], sk["splits"]) == (4, 4)
+    untuned = gr.selected_splitk_config(2048, 2048, 2048 + 8, splits=4)
+    assert (untuned["config_id"], untuned["splits"]) == (4, 4)
+    # the skinny shape with B stored (N, K) is tuned unsplit on the 64x64 producer tile; asked for
+    # 2 parts it takes the 64x256 tile of the size rules for M <= 64
+    sk = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16, splits=2, b_layout=gr.B_NK)
+    assert (sk["config_id"], sk["splits"]) == (6, 2)
+    # with the parts left to the library, the table still decides
+    sk = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16, b_layout=gr.B_NK)
+    assert (sk["config_id"], sk["splits"]) == (9, 1)
+    # a tuned row whose split-K tile does split keeps it for explicit parts (deep K: 64x64, 4 parts)
+    sk = gr.selected_splitk_config(512, 512, 16384, splits=2)
+    assert (sk["config_id"], sk["splits"]) == (5, 2)

@@ -6,6 +6,7 @@ from .binding import (  # noqa: F401
     selected_splitk_config,
     gemm_relu_raw,
     selected_config,
+    selected_block_config,
     strerror,
     library_path,
     load_library,

@@ -93,6 +93,9 @@ def load_library():
             lib.gemm_relu_query_splitk.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci,
                                                    ctypes.POINTER(_Config)]
             lib.gemm_relu_query_splitk.restype = ci
+            ip = ctypes.POINTER(ci)
+            lib.gemm_relu_selected_config.argtypes = [i64, i64, i64, ci, ip, ip, ip, ip]
+            lib.gemm_relu_selected_config.restype = ci
             lib.gemm_relu_strerror.argtypes = [ci]
             lib.gemm_relu_strerror.restype = ctypes.c_char_p
             lib.gemm_relu_version.argtypes = []
@@ -280,3 +283,11 @@ def selected_config(M: int, N: int, K: int, dtype: int = F16, config: int = CONF
                                            ctypes.byref(cfg))
     _check(rc)
     return {f: getattr(cfg, f) for f, _ in _Config._fields_}
+
+
+def selected_block_config(M: int, N: int, K: int, dtype: int = F16) -> tuple:
+    """(block_m, block_n, block_k, stages) that gemm_relu picks for dense, 256-byte aligned buffers
+    (gemm_relu_selected_config; host logic only)."""
+    out = [ctypes.c_int(-1) for _ in range(4)]
+    _check(load_library().gemm_relu_selected_config(M, N, K, dtype, *(ctypes.byref(v) for v in out)))
+    return tuple(v.value for v in out)

@@ -2,6 +2,7 @@
 // launch.  The operation and its contract are documented in gemm_relu.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -141,10 +142,20 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     const bool dword_vectors = va >= 2 && vb >= 2;
     int chosen = config_id;
     // A tuned shape, with pointers aligned as the tuner's were: its measured best.
+    // An explicit number of parts keeps the tuned split-K tile only if that
+    // tile has split-K kernels; otherwise the size rules below pick one that
+    // does, so the request is never dropped.
     if (chosen == GEMM_RELU_CONFIG_AUTO && va == row_width(K) && vb == row_width(plan->b_nk ? K : N)) {
         if (const TunedShape* t = find_tuned(M, N, K, dtype, b_layout)) {
-            chosen = splits_req >= 0 ? t->splitk_config : t->config;
-            if (splits_req == 0) splits_req = t->splits;
+            if (splits_req < 0) {
+                chosen = t->config;
+            } else if (splits_req == 0) {
+                chosen = t->splitk_config;
+                splits_req = t->splits;
+            } else if (t->splitk_config >= GEMM_RELU_CONFIG_DMA_256 &&
+                       has_splitk(t->splitk_config - GEMM_RELU_CONFIG_DMA_256)) {
+                chosen = t->splitk_config;
+            }
         }
     }
     // With split-K on offer, a block of at most 64 rows takes the 64x256 tile:
@@ -396,6 +407,28 @@ int gemm_relu_query_config(const void* A, const void* B, const void* C, int64_t 
                            int dtype, int config_id, gemm_relu_config_t* out)
 {
     return gemm_relu_query_config_ex(A, B, C, M, N, K, dtype, GEMM_RELU_B_KN, config_id, out);
+}
+
+int gemm_relu_selected_config(int64_t M, int64_t N, int64_t K, int dtype, int* bm, int* bn, int* bk, int* stages)
+{
+    // gemm_relu's choice for dense 256-byte aligned, non-overlapping buffers
+    // (what a device allocator returns).  The addresses are never dereferenced:
+    // they only feed the alignment and overlap checks.
+    const uintptr_t kBase = 256;
+    auto round_up = [](int64_t bytes) { return (uintptr_t)((std::max<int64_t>(bytes, 0) + 255) / 256 * 256); };
+    const uintptr_t a = kBase;
+    const uintptr_t b = a + round_up(2 * M * K);
+    const uintptr_t c = b + round_up(2 * K * N);
+    Plan p;
+    const int rc = make_plan(reinterpret_cast<const void*>(a), reinterpret_cast<const void*>(b),
+                             reinterpret_cast<const void*>(c), M, N, K, dtype, GEMM_RELU_B_KN,
+                             GEMM_RELU_CONFIG_AUTO, -1, &p);
+    if (rc != GEMM_RELU_OK) return rc;
+    if (bm) *bm = p.cfg.block_m;
+    if (bn) *bn = p.cfg.block_n;
+    if (bk) *bk = p.cfg.block_k;
+    if (stages) *stages = p.cfg.stages;
+    return GEMM_RELU_OK;
 }
 
 int gemm_relu_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
