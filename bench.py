@@ -17,7 +17,6 @@ import argparse
 import json
 import os
 import re
-import subprocess
 import sys
 import threading
 import time
@@ -73,26 +72,66 @@ def make_sets(w, n_sets, device, b_layout=binding.B_KN):
     return sets
 
 
-def sample_clocks(launch, seconds):
-    """Keep the GPU busy with `launch` for about `seconds` while rocm-smi samples the shader
-    and memory clocks (and the package power where the board reports it).  Returns medians
-    over the samples after the first, or None if rocm-smi is unavailable."""
+def _gpu_sysfs_dir():
+    """The sysfs device directory of the GPU (AMD vendor id with a shader-clock table), or None."""
+    import glob
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            if open(os.path.join(d, "vendor")).read().strip() == "0x1002" and \
+                    os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                return d
+        except OSError:
+            continue
+    return None
+
+
+_SYSFS = None
+
+
+def read_clocks():
+    """Current shader and memory clock (MHz) and package power (W) from the driver's sysfs files:
+    the active level of pp_dpm_sclk / pp_dpm_mclk (the level marked '*'; on these boards the
+    middle level carries the live frequency) and hwmon power1_average or power1_input.  A field
+    the board does not report is "unavailable"."""
+    global _SYSFS
+    if _SYSFS is None:
+        _SYSFS = _gpu_sysfs_dir() or ""
+    out = {"sclk_mhz": "unavailable", "mclk_mhz": "unavailable", "power_w": "unavailable"}
+    if not _SYSFS:
+        return out
+    for key, name in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+        try:
+            for line in open(os.path.join(_SYSFS, name)):
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    if m:
+                        out[key] = int(m.group(1))
+        except OSError:
+            pass
+    import glob
+    for f in sorted(glob.glob(os.path.join(_SYSFS, "hwmon", "hwmon*", "power1_average")) +
+                    glob.glob(os.path.join(_SYSFS, "hwmon", "hwmon*", "power1_input"))):
+        try:
+            uw = int(open(f).read().strip())
+        except (OSError, ValueError):
+            continue
+        if uw > 0:
+            out["power_w"] = round(uw / 1e6, 1)
+            break
+    return out
+
+
+def sample_clocks(launch, seconds, interval=0.02):
+    """Keep the GPU busy with `launch` for about `seconds` while the clocks (and power, where the
+    board reports it) are read every `interval` s.  Returns medians and ranges over the samples."""
     samples, stop = [], threading.Event()
 
-    def smi():
+    def reader():
         while not stop.is_set():
-            try:
-                out = subprocess.run(["rocm-smi", "--showclocks", "--showpower"], capture_output=True,
-                                     text=True, timeout=10).stdout
-            except (OSError, subprocess.SubprocessError):
-                return
-            clk = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
-            mclk = re.search(r"mclk clock level: \d+: \((\d+)Mhz\)", out)
-            pwr = re.search(r"(?<!Max )Graphics Package Power \(W\): ([0-9.]+)", out)
-            samples.append((int(clk.group(1)) if clk else None, float(pwr.group(1)) if pwr else None,
-                            int(mclk.group(1)) if mclk else None))
+            samples.append(read_clocks())
+            time.sleep(interval)
 
-    th = threading.Thread(target=smi, daemon=True)
+    th = threading.Thread(target=reader, daemon=True)
     th.start()
     t0, i = time.time(), 0
     while time.time() - t0 < seconds:
@@ -101,24 +140,31 @@ def sample_clocks(launch, seconds):
             i += 1
         torch.cuda.synchronize()
     stop.set()
-    th.join(timeout=15)
-    clks = sorted(c for c, _, _ in samples[1:] if c is not None)
-    pwrs = sorted(p for _, p, _ in samples[1:] if p is not None)
-    mclks = sorted(m for _, _, m in samples[1:] if m is not None)
-    if not clks:
-        return None
-    return {"sclk_mhz_median": clks[len(clks) // 2], "sclk_mhz_min": clks[0], "sclk_mhz_max": clks[-1],
-            "mclk_mhz_median": mclks[len(mclks) // 2] if mclks else None,
-            "power_w_median": pwrs[len(pwrs) // 2] if pwrs else None, "samples": len(clks),
-            "seconds": round(time.time() - t0, 2), "source": "rocm-smi --showclocks --showpower"}
+    th.join(timeout=5)
+    n_skip = len(samples) // 10                  # the first tenth: the clock still settling
+    body = samples[n_skip:] or samples
+
+    def summary(key):
+        vals = sorted(v[key] for v in body if not isinstance(v[key], str))
+        if not vals:
+            return "unavailable"
+        return {"median": vals[len(vals) // 2], "min": vals[0], "max": vals[-1]}
+
+    return {"sclk_mhz": summary("sclk_mhz"), "mclk_mhz": summary("mclk_mhz"), "power_w": summary("power_w"),
+            "samples": len(body), "seconds": round(time.time() - t0, 2),
+            "source": "sysfs pp_dpm_sclk / pp_dpm_mclk, hwmon power1_*"}
 
 
 def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN,
-                  splits=None, clock_seconds=0.0):
-    """Returns (ms per step over the timed region of K back-to-back launches, mean ms per launch
-    between per-launch events in a second pass, clock samples or None).  splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with
-    that many parts.  clock_seconds > 0: after the timed region, keep launching for that long while
-    rocm-smi samples the clock (outside the timed region)."""
+                  splits=None, repeats=1, per_launch_pass=False, clock_seconds=0.0):
+    """Time one workload.  After `warmup` untimed launches, `repeats` timed regions of exactly
+    `steps` back-to-back launches each, every region bracketed by a device synchronisation and a
+    pair of GPU events on the launch stream.  Returns a dict with the median region's ms per step
+    and every region's, the clocks read right before the first and right after the last region,
+    optionally the mean ms per launch of a pass with a pair of events around every launch, and,
+    with clock_seconds > 0, clocks sampled while the workload runs on for that long (outside the
+    timed regions).  splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with
+    that many parts."""
     sets = make_sets(w, n_sets, device, b_layout)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
@@ -147,61 +193,37 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
         launch(i)
     torch.cuda.synchronize(device)
 
-    # Timed region: K back-to-back launches between two events, nothing else on the
-    # stream.  In the kernel trace they follow each other with no gap and no
-    # overlap, so the region's length over K is both the time per step and each
-    # launch's average duration.
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(device)
-    t0.record(stream)
-    for i in range(steps):
-        launch(i)
-    t1.record(stream)
-    torch.cuda.synchronize(device)
-    step_ms = t0.elapsed_time(t1) / steps
-    # Then the same K launches once more, each between its own pair of events on
-    # the launch stream: the per-launch durations.  The event records add host
-    # time to every launch and leave about 10 us between launches on the GPU
-    # (which sets the pace of small shapes), so this pass is reported beside the
-    # step time, not used as it.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        launch(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize(device)
-    kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
-    clocks = sample_clocks(launch, clock_seconds) if clock_seconds > 0 else None
-    del sets
-    return step_ms, kernel_ms, clocks
-
-
-def time_vendor(w, steps, warmup, n_sets, device):
-    """The same workload through the vendor library in one process: torch.mm (hipBLASLt on
-    ROCm) alone, and followed by an in-place ReLU (two kernels).  Mean ms per step between GPU
-    events.  For context only: nothing in the library uses it."""
-    sets = make_sets(w, n_sets, device)
-    stream = torch.cuda.current_stream(device)
-    out = {}
-    for name, relu in (("mm_ms", False), ("mm_relu_ms", True)):
-        def step(i):
-            a, b, c = sets[i % n_sets]
-            torch.mm(a, b, out=c)
-            if relu:
-                torch.relu_(c)
-        for i in range(warmup):
-            step(i)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed regions: K back-to-back launches between two events, nothing else on the stream.
+    # In the kernel trace they follow each other with no gap and no overlap, so a region's
+    # length over K is both the time per step and each launch's average duration.
+    before = read_clocks()
+    region_ms = []
+    for _ in range(repeats):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize(device)
         t0.record(stream)
         for i in range(steps):
-            step(i)
+            launch(i)
         t1.record(stream)
         torch.cuda.synchronize(device)
-        out[name] = round(t0.elapsed_time(t1) / steps, 5)
-    out["mm_tflops"] = round(w.flop / (out["mm_ms"] * 1e-3) / 1e12, 1)
-    out["mm_relu_tflops"] = round(w.flop / (out["mm_relu_ms"] * 1e-3) / 1e12, 1)
+        region_ms.append(t0.elapsed_time(t1) / steps)
+    after = read_clocks()
+    out = {"ms_per_step": sorted(region_ms)[len(region_ms) // 2], "region_ms_per_step": region_ms,
+           "clocks_before": before, "clocks_after": after}
+    if per_launch_pass:
+        # The same K launches once more, each between its own pair of events on the launch
+        # stream.  The event records add host time to every launch and leave about 10 us
+        # between launches on the GPU, which sets the pace of the small shapes.
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            launch(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize(device)
+        out["ms_per_launch_between_events"] = sum(s.elapsed_time(e) for s, e in ev) / steps
+    if clock_seconds > 0:
+        out["clocks_sustained"] = sample_clocks(launch, clock_seconds)
     del sets
     return out
 
@@ -296,6 +318,8 @@ def main():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--repeats", type=int, default=5,
+                   help="timed regions of --steps launches each; the median region is reported")
     p.add_argument("--workload", default="square_8192", choices=sorted(inputs.WORKLOADS))
     p.add_argument("--sets", type=int, default=3, help="rotated input/output sets")
     p.add_argument("--config", type=int, default=binding.CONFIG_AUTO)
@@ -304,11 +328,9 @@ def main():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
-    p.add_argument("--no-vendor", action="store_true",
-                   help="skip timing the same workload through torch.mm (+ torch.relu_)")
     p.add_argument("--clock-seconds", type=float, default=2.0,
-                   help="after the timed steps, sustain the workload this long while rocm-smi samples the "
-                        "shader clock (0: skip)")
+                   help="after the timed steps, sustain the workload this long while the shader clock "
+                        "is sampled (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = p.parse_args()
@@ -316,6 +338,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
               "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.repeats < 1 or args.warmup < 0:
+        print("bench.py: --steps and --repeats must be >= 1, --warmup >= 0", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -332,15 +357,17 @@ def main():
     cfg = gr.selected_config(w.M, w.N, w.K, binding.F16 if w.dtype == "fp16" else binding.BF16, args.config,
                              b_layout=b_layout)
     log(f"[bench] {w.name}: config {cfg}")
-    ms_step, kernel_ms_events, clocks = time_workload(w, args.steps, args.warmup, args.sets, device, args.config,
-                                                      b_layout, clock_seconds=args.clock_seconds)
-    log(f"[bench] clocks under sustained load: {clocks}")
+    head = time_workload(w, args.steps, args.warmup, args.sets, device, args.config, b_layout,
+                         repeats=args.repeats, clock_seconds=args.clock_seconds)
+    ms_step = head["ms_per_step"]
     # One launch per step, back to back with no gap: the step time is the kernel's
     # average launch duration over the timed region.
     tflops = w.flop / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log(f"[bench] {w.name}: {ms_step:.4f} ms/step, {tflops:.1f} TFLOP/s; "
-        f"{kernel_ms_events:.4f} ms per launch between per-launch events")
+    log(f"[bench] {w.name}: median {ms_step:.4f} ms/step over {args.repeats} regions "
+        f"{[round(x, 4) for x in head['region_ms_per_step']]}, {tflops:.1f} TFLOP/s; "
+        f"clocks before {head['clocks_before']}, after {head['clocks_after']}")
+    log(f"[bench] clocks under sustained load: {head.get('clocks_sustained')}")
 
     secondary = {}
     if not args.no_secondary:
@@ -348,49 +375,38 @@ def main():
         runs = [("small_256", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("square_1024", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, None),     # the pages' 128x128x64 tile
-                ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, 4),
                 ("ragged_4000x11000x4100", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_DMA_64x256, 4),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
                 ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None),
-                ("square_8192_bf16", binding.B_KN, binding.CONFIG_AUTO, None),
-                ("square_8192", binding.B_KN, binding.CONFIG_DMA_256x128_WS, None)]
+                ("square_8192_bf16", binding.B_KN, binding.CONFIG_AUTO, None)]
         for name, s_layout, s_config, s_splits in runs:
             sw = inputs.WORKLOADS[name]
             if (sw.name == w.name and s_splits is None and s_config == binding.CONFIG_AUTO and
                     args.b_layout == ("nk" if s_layout == binding.B_NK else "kn")):
                 continue
-            s_ms, s_kms, _ = time_workload(sw, 50 if sw.flop < 1e12 else 20, 50, 3, device, config=s_config,
-                                           b_layout=s_layout, splits=s_splits)
+            r = time_workload(sw, 50 if sw.flop < 1e12 else 20, 50, 3, device, config=s_config,
+                              b_layout=s_layout, splits=s_splits, repeats=3, per_launch_pass=True)
+            s_ms, s_kms = r["ms_per_step"], r["ms_per_launch_between_events"]
             if s_layout == binding.B_NK:
                 name += "_b_nk"
             if s_splits is not None:
                 name += "_splitk" if s_config == binding.CONFIG_AUTO else f"_splitk{s_splits}_config{s_config}"
             elif s_config != binding.CONFIG_AUTO:
                 name += "_" + binding.CONFIG_NAMES[s_config]
-            entry = {"ms": round(s_kms, 5), "ms_per_step_batch": round(s_ms, 5),
-                     "TFLOP/s": round(sw.flop / (s_kms * 1e-3) / 1e12, 2),
-                     "frac_mfma_peak": round(sw.flop / (s_kms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
-                     "GB/s": round(sw.bytes_once / (s_kms * 1e-3) / 1e9, 1)}
+            # Rates from the back-to-back step time (the median of 3 regions).  On the small
+            # shapes the gap between back-to-back launches is part of it; the per-launch time
+            # between events is given beside it.
+            entry = {"ms_per_step": round(s_ms, 5), "ms_per_launch_between_events": round(s_kms, 5),
+                     "TFLOP/s": round(sw.flop / (s_ms * 1e-3) / 1e12, 2),
+                     "frac_mfma_peak": round(sw.flop / (s_ms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
+                     "GB/s": round(sw.bytes_once / (s_ms * 1e-3) / 1e9, 1),
+                     "sclk_mhz_after": r["clocks_after"]["sclk_mhz"]}
             entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
-            if not args.no_vendor and s_layout == binding.B_KN and s_config == binding.CONFIG_AUTO and s_splits is None:
-                # The same workload through torch.mm + torch.relu_ in this process, per step
-                # (back-to-back launches, launch gaps included on both sides, no per-launch
-                # events on either): context, not a target.
-                v = time_vendor(sw, 50 if sw.flop < 1e12 else 20, 50, 3, device)
-                entry["vendor_mm_relu_ms"] = v["mm_relu_ms"]
-                entry["fused_step_vs_mm_relu"] = round(v["mm_relu_ms"] / s_ms, 3)
             secondary[name] = entry
             log(f"[bench] {name}: {entry}")
-
-    vendor = None
-    if not args.no_vendor:
-        vendor = time_vendor(w, args.steps, args.warmup, args.sets, device)
-        # Both timed the same way: back-to-back steps, no per-launch events.
-        vendor["fused_step_vs_mm_relu"] = round(vendor["mm_relu_ms"] / ms_step, 3)
-        log(f"[bench] vendor library (torch.mm, then torch.relu_): {vendor}")
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -410,8 +426,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": args.repeats,
         "ms_per_step": round(ms_step, 5),
-        "ms_per_launch_between_events": round(kernel_ms_events, 5),
+        "region_ms_per_step": [round(x, 5) for x in head["region_ms_per_step"]],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -429,8 +446,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "kernel_source_sha256": kernel_source_digest(),
-        "clocks": clocks,
-        "vendor_reference": vendor,
+        "clocks": {"before_timed_regions": head["clocks_before"], "after_timed_regions": head["clocks_after"],
+                   "sustained": head.get("clocks_sustained")},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

@@ -25,7 +25,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_help_lists_the_contract_flags():
     res = run("--help")
     assert res.returncode == 0
-    for flag in ("--gpus", "--steps", "--warmup", "--workload", "--b-layout", "--clock-seconds", "--no-vendor"):
+    for flag in ("--gpus", "--steps", "--warmup", "--repeats", "--workload", "--b-layout", "--clock-seconds"):
         assert flag in res.stdout
 
 
@@ -34,8 +34,8 @@ def test_bench_prints_the_contract_line():
     # A short run on the 256^3 workload: one JSON line with the contract's fields;
     # the timed region is K back-to-back launches, so the kernel's average launch
     # duration over it gives roofline.achieved == value.
-    res = run("--workload", "small_256", "--steps", "5", "--warmup", "5", "--no-cpu-baseline", "--no-secondary",
-              "--no-vendor", "--clock-seconds", "0")
+    res = run("--workload", "small_256", "--steps", "5", "--warmup", "5", "--repeats", "3", "--no-cpu-baseline",
+              "--no-secondary", "--clock-seconds", "0")
     assert res.returncode == 0, res.stderr[-2000:]
     lines = [l for l in res.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1
@@ -49,4 +49,13 @@ def test_bench_prints_the_contract_line():
     r = j["roofline"]
     assert (r["bound"], r["unit"], r["peak"]) == ("mfma", "TFLOP/s", 2500.0)
     assert r["achieved"] == j["value"] and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
-    assert j["ms_per_launch_between_events"] > 0
+    # the median of the timed regions, each of exactly `steps` launches
+    assert j["repeats"] == 3 and len(j["region_ms_per_step"]) == 3
+    assert j["ms_per_step"] == sorted(j["region_ms_per_step"])[1]
+    for side in ("before_timed_regions", "after_timed_regions"):
+        assert set(j["clocks"][side]) == {"sclk_mhz", "mclk_mhz", "power_w"}
+
+
+def test_zero_repeats_are_refused():
+    res = run("--repeats", "0")
+    assert res.returncode == 2

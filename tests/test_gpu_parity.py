@@ -309,6 +309,35 @@ def test_k_straddling_piece(shape, a_off):
             assert bad.size == 0, (dtype, config, f"{len(bad)} differ, first at {tuple(bad[0])}")
 
 
+@pytest.mark.parametrize("b_layout", [binding.B_KN, binding.B_NK])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_producer_wave_tiles_with_more_tiles_than_cus(dtype, b_layout):
+    # The producer-wave configs with more output tiles than persistent workgroups: every
+    # workgroup runs several tiles, so the producer waves set up the next tile's loads while
+    # the compute waves run the last tile's epilogue (staged through LDS for the 128x128
+    # tile).  M, N and K tails (K % 64 = 8).  AUTO picks the 128x128 producer tile here.
+    M, N, K = 2056, 2312, 200
+    a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=M + N + K + b_layout)
+    want = oracle.gemm_relu(a, b, dtype)
+    bd = (b.t().contiguous() if b_layout == binding.B_NK else b).cuda()
+    ad = a.cuda()
+    code = gr.F16 if dtype == "fp16" else gr.BF16
+    for config in (binding.CONFIG_DMA_32x32_WS, binding.CONFIG_DMA_64x64_WS, binding.CONFIG_DMA_128x128_WS,
+                   binding.CONFIG_AUTO):
+        cfg = gr.selected_config(M, N, K, dtype=code, config=config, b_layout=b_layout)
+        if config == binding.CONFIG_AUTO:
+            assert cfg["config_id"] == binding.CONFIG_DMA_128x128_WS
+        else:
+            assert cfg["config_id"] == config
+        assert cfg["grid"] > 256, cfg
+        say(f"[producer tiles] {M}x{N}x{K} {dtype} layout={b_layout} config={cfg['config_id']} tiles={cfg['grid']}")
+        c = gr.gemm_relu_ex(ad, bd, b_layout=b_layout, config=config)
+        torch.cuda.synchronize()
+        got = bits(c)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (config, f"{len(bad)} differ, first at {tuple(bad[0])}")
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("config", CONFIGS)
 def test_subnormal_inputs(config, dtype):
