@@ -17,7 +17,8 @@
  * Memory: A, B and C are device pointers owned by the caller (e.g. torch
  * allocations).  The library allocates nothing and keeps no state between
  * calls except a per-device cache of the device's architecture (split-K takes
- * a caller-owned workspace).
+ * a caller-owned workspace; its no-allocation variant uses a static device
+ * array that the library's code object holds on each device).
  *
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL means the null
  * stream) and the call returns without waiting.  C is complete once the
@@ -62,7 +63,9 @@ enum {
     GEMM_RELU_ERR_TOO_LARGE = -7,   /* a dimension or an addressed band exceeds the limits above */
     GEMM_RELU_ERR_BAD_CONFIG = -8,  /* an unknown kernel configuration id */
     GEMM_RELU_ERR_BAD_LAYOUT = -9,  /* b_layout is neither GEMM_RELU_B_KN nor GEMM_RELU_B_NK */
-    GEMM_RELU_ERR_WORKSPACE = -10   /* split-K workspace missing, too small or not 256-byte aligned */
+    GEMM_RELU_ERR_WORKSPACE = -10,  /* split-K workspace missing, too small or not 256-byte aligned */
+    GEMM_RELU_ERR_SCRATCH = -11     /* gemm_relu_splitk_noalloc: the call needs more than the
+                                       library's static scratch (GEMM_RELU_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* How B is stored (gemm_relu_ex).  The operation is C = ReLU(A @ B) with B of
@@ -241,6 +244,34 @@ int gemm_relu_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N
  * `splits` and `workspace_bytes`.  `out` may be NULL. */
 int gemm_relu_query_splitk(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
                            int dtype, int b_layout, int config_id, int splits, gemm_relu_config_t* out);
+
+/* Size of the device array gemm_relu_splitk_noalloc uses as its workspace: the
+ * 64 KiB counter region plus 32 MiB of fp32 partial tiles. */
+#define GEMM_RELU_NOALLOC_SCRATCH_BYTES ((int64_t)65536 + ((int64_t)32 << 20))
+
+/*
+ * gemm_relu_splitk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split-K partials and counters live
+ * in a static device array of GEMM_RELU_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends; the call allocates
+ * nothing and calls no allocating routine.  The caller still passes A, B and C.
+ *
+ * Arguments, results and errors are those of gemm_relu_splitk with the
+ * workspace removed; a call whose gemm_relu_query_splitk workspace_bytes
+ * exceed GEMM_RELU_NOALLOC_SCRATCH_BYTES returns GEMM_RELU_ERR_SCRATCH before
+ * anything is launched (ask for fewer parts).  When the split resolves to 1
+ * part the call is gemm_relu_ex and the array is not touched.  Each split call
+ * first clears the counters it uses (a small fill kernel on `stream`, ordered
+ * before the GEMM), so the array's previous contents never matter.
+ *
+ * The array is shared by every call on a device: calls that may overlap in
+ * time on one device (different streams, or different host threads without
+ * ordering) race and give wrong results; order them on one stream.  The first
+ * call on a device looks up the array's address; make it before graph capture.
+ */
+int gemm_relu_splitk_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                             int dtype, int b_layout, int config_id, int splits, void* stream);
 
 /* A static, human-readable description of a return code.  The pages' GEMM
  * surfaces its failures at two points, when the kernel is built (layout and

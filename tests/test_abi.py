@@ -31,7 +31,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gemm_relu", "gemm_relu_with_config", "gemm_relu_query_config", "gemm_relu_strerror",
         "gemm_relu_version", "gemm_relu_ex", "gemm_relu_query_config_ex", "gemm_relu_splitk",
-        "gemm_relu_query_splitk", "gemm_relu_selected_config"])
+        "gemm_relu_query_splitk", "gemm_relu_selected_config", "gemm_relu_splitk_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -342,3 +342,27 @@ def test_explicit_parts_are_never_dropped_by_the_tuned_table():
     # a tuned row whose split-K tile does split keeps it for explicit parts (deep K: 64x64, 4 parts)
     sk = gr.selected_splitk_config(512, 512, 16384, splits=2)
     assert (sk["config_id"], sk["splits"]) == (5, 2)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    # gemm_relu_splitk_noalloc keeps partials in a static device array; a call needing more is
+    # refused on the host before anything is launched (no device is touched here).
+    args = (A_PTR, B_PTR, C_PTR, 8192, 8192, 1024, 0, 0, 4)      # 128x128 tiles, forced
+    need = gr.selected_splitk_config(8192, 8192, 1024, config=4, splits=2)
+    assert need["splits"] == 2 and need["workspace_bytes"] > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.gemm_relu_splitk_noalloc(*args, 2, None) == -11
+    assert "scratch" in gr.strerror(-11)
+    # the usual argument errors come first
+    assert lib.gemm_relu_splitk_noalloc(A_PTR, B_PTR, C_PTR, 64, 512, 512, 9, 0, -1, 4, None) == -2
+    assert lib.gemm_relu_splitk_noalloc(A_PTR, B_PTR, C_PTR, 64, 512, 512, 0, 0, -1, 65, None) == -1
+    assert lib.gemm_relu_splitk_noalloc(A_PTR, B_PTR, A_PTR + 2, 64, 512, 512, 0, 0, -1, 4, None) == -3
+    # M == 0: nothing to do, no device needed
+    assert lib.gemm_relu_splitk_noalloc(0, 0, 0, 0, 512, 512, 0, 0, -1, 4, None) == 0
+    # the header's size is the binding's
+    text = open(HEADER).read()
+    assert "#define GEMM_RELU_NOALLOC_SCRATCH_BYTES ((int64_t)65536 + ((int64_t)32 << 20))" in text
+    # every shape the library splits by itself fits (at most ~256 units of partial tiles)
+    for shape in [(64, 16384, 8192, 1), (512, 512, 16384, 0), (1024, 1024, 1024, 0), (2000, 1500, 4096, 0)]:
+        M, N, K, dt = shape
+        cfg = gr.selected_splitk_config(M, N, K, dtype=dt)
+        assert cfg["workspace_bytes"] <= binding.NOALLOC_SCRATCH_BYTES, shape

@@ -3,6 +3,7 @@ from .binding import (  # noqa: F401
     gemm_relu,
     gemm_relu_ex,
     gemm_relu_splitk,
+    gemm_relu_splitk_noalloc,
     selected_splitk_config,
     gemm_relu_raw,
     selected_config,

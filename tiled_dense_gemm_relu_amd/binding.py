@@ -38,8 +38,11 @@ CONFIG_NAMES = {CONFIG_DIRECT: "direct_32x32", CONFIG_TILE_256: "tile_256x256x64
 
 ERRORS = {
     0: "OK", -1: "INVALID_ARG", -2: "BAD_DTYPE", -3: "ALIAS", -4: "MISALIGNED", -5: "NO_DEVICE",
-    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG", -9: "BAD_LAYOUT", -10: "WORKSPACE",
+    -6: "LAUNCH", -7: "TOO_LARGE", -8: "BAD_CONFIG", -9: "BAD_LAYOUT", -10: "WORKSPACE", -11: "SCRATCH",
 }
+
+# GEMM_RELU_NOALLOC_SCRATCH_BYTES: the static device array gemm_relu_splitk_noalloc works in.
+NOALLOC_SCRATCH_BYTES = 65536 + (32 << 20)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
@@ -93,6 +96,8 @@ def load_library():
             lib.gemm_relu_query_splitk.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci,
                                                    ctypes.POINTER(_Config)]
             lib.gemm_relu_query_splitk.restype = ci
+            lib.gemm_relu_splitk_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, vp]
+            lib.gemm_relu_splitk_noalloc.restype = ci
             ip = ctypes.POINTER(ci)
             lib.gemm_relu_selected_config.argtypes = [i64, i64, i64, ci, ip, ip, ip, ip]
             lib.gemm_relu_selected_config.restype = ci
@@ -258,6 +263,28 @@ def gemm_relu_splitk(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_
     with torch.cuda.device(a.device):
         rc = lib.gemm_relu_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype, b_layout, config,
                                   splits, ws_ptr, ws_bytes, s.cuda_stream or None)
+    _check(rc)
+    return out
+
+
+def gemm_relu_splitk_noalloc(a, b, out=None, b_layout: int = B_KN, config: int = CONFIG_AUTO, splits: int = 0,
+                             stream=None):
+    """gemm_relu_splitk with the library's static device scratch instead of a workspace (the C
+    entry point allocates nothing; here ``out`` is allocated if not given).  Calls that may overlap
+    in time on one device share that scratch and race: keep them on one stream."""
+    import torch
+    if b_layout not in (B_KN, B_NK):
+        raise ValueError(f"gemm_relu: b_layout must be B_KN or B_NK, got {b_layout}")
+    dev = _check_tensors(a, b, out, b_layout)
+    dtype = _dtype_code(a)
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    handle = _stream_handle(stream, dev)
+    with torch.cuda.device(a.device):
+        rc = load_library().gemm_relu_splitk_noalloc(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, dtype,
+                                                     b_layout, config, splits, handle or None)
     _check(rc)
     return out
 

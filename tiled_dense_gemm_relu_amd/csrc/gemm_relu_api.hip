@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gemm_relu.h"
 #include "kernel_table.hpp"
@@ -314,6 +315,35 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     return GEMM_RELU_OK;
 }
 
+// The split-K scratch of gemm_relu_splitk_noalloc: the fixed counter region,
+// then room for the fp32 partial tiles.  One copy per device, held for the life
+// of the process; every call on a device shares it.  In host code `scratch`
+// names a host-side stand-in, never the device memory: kernels and copies get
+// the address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchBytes = GEMM_RELU_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > kCounterBytes && kScratchBytes % 256 == 0, "scratch layout");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64];   // per device, under g_scratch_mutex
+
+// The device address of this device's scratch array, looked up once per device
+// with that device current.
+int device_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_RELU_ERR_NO_DEVICE;
+    if (dev >= 64) return GEMM_RELU_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GEMM_RELU_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GEMM_RELU_OK;
+}
+
 // Per-device cache: 0 unknown, > 0 gfx950 with that many CUs, -1 something else.
 std::atomic<int> g_device_cus[64];
 
@@ -479,6 +509,32 @@ int gemm_relu_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N
     return run(p, A, B, C, M, N, K, dtype, workspace, stream);
 }
 
+int gemm_relu_splitk_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                             int b_layout, int config_id, int splits, void* stream)
+{
+    Plan p;
+    const int rc = make_plan(A, B, C, M, N, K, dtype, b_layout, config_id, splits < 0 ? -2 : splits, &p);
+    if (rc != GEMM_RELU_OK) return rc;
+    if (p.splits <= 1) return run(p, A, B, C, M, N, K, dtype, nullptr, stream);
+    if (p.cfg.workspace_bytes > kScratchBytes) return GEMM_RELU_ERR_SCRATCH;
+    int cus = 0;
+    int status = check_device(&cus);
+    if (status != GEMM_RELU_OK) return status;
+    void* ws = nullptr;
+    status = device_scratch(&ws);
+    if (status != GEMM_RELU_OK) return status;
+    // The counters this call uses (one int per tile and wave) start at zero:
+    // cleared by a fill kernel (not a memset node, so the call stays capturable),
+    // ordered before the GEMM on the same stream.
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    size_t halves = (size_t)p.tiles_m * (size_t)p.tiles_n * (size_t)(p.cfg.threads / 64) * 2;
+    void* fill_args[] = {&ws, &halves};
+    const unsigned fill_grid = (unsigned)std::min<size_t>((halves + 255) / 256, 65536);
+    if (hipLaunchKernel(zero_fill_kernel(), dim3(fill_grid), dim3(256), fill_args, 0, s) != hipSuccess)
+        return GEMM_RELU_ERR_LAUNCH;
+    return launch(p, A, B, C, M, N, K, dtype, cus, ws, s);
+}
+
 const char* gemm_relu_strerror(int code)
 {
     switch (code) {
@@ -493,6 +549,8 @@ const char* gemm_relu_strerror(int code)
     case GEMM_RELU_ERR_BAD_CONFIG: return "unknown kernel configuration id";
     case GEMM_RELU_ERR_BAD_LAYOUT: return "unknown B layout (expected GEMM_RELU_B_KN or GEMM_RELU_B_NK)";
     case GEMM_RELU_ERR_WORKSPACE: return "split-K workspace missing, too small or not 256-byte aligned";
+    case GEMM_RELU_ERR_SCRATCH:
+        return "split-K partials of this call exceed the library's static scratch (gemm_relu_splitk_noalloc)";
     default: return "unknown error code";
     }
 }
