@@ -36,7 +36,7 @@ HIPCC_FLAGS = [
 ]
 
 
-KERNEL_SOURCES = ["gemm_relu_kernels.hpp", "kernels_f16.hip", "kernels_bf16.hip"]
+KERNEL_SOURCES = ["gemm_relu_kernels.hpp", "kernel_instances.hpp", "kernels_f16.hip", "kernels_bf16.hip"]
 
 
 def kernel_source_digest() -> str:

@@ -1,117 +1,11 @@
 // Instances of the gfx950 GEMM + ReLU kernels for the f16 dtype.
-#include "gemm_relu_kernels.hpp"
-#include "kernel_table.hpp"
+#include "kernel_instances.hpp"
 
 namespace gemm_relu_hip {
 
-namespace {
-using Tile256 = TileConfig<256, 256, 2, 2, 8>;
-using Tile128 = TileConfig<128, 128, 2, 2, 8>;
-
-template <class Cfg, int id>
-constexpr bool geom_matches = Cfg::BM == kTileGeom[id].bm && Cfg::BN == kTileGeom[id].bn &&
-                              Cfg::BK == kTileGeom[id].bk && Cfg::STAGES == kTileGeom[id].stages &&
-                              Cfg::THREADS == kTileGeom[id].threads && Cfg::GROUP_M == kTileGeom[id].group_m;
-static_assert(geom_matches<Tile256, kTile256> && geom_matches<Tile128, kTile128>,
-              "host tile table out of date");
-template <class Cfg, int id>
-constexpr bool dma_geom_matches = Cfg::BM == kDmaGeom[id].bm && Cfg::BN == kDmaGeom[id].bn &&
-                                  Cfg::BK == kDmaGeom[id].bk && Cfg::STAGES == kDmaGeom[id].stages &&
-                                  Cfg::THREADS == kDmaGeom[id].threads && Cfg::GROUP_M == kDmaGeom[id].group_m &&
-                                  Cfg::C_STAGE_BYTES == kDmaGeom[id].c_stage;
-template <class Cfg>
-constexpr bool dw_geom_matches = Cfg::BM == kDma256DwGeom.bm && Cfg::BN == kDma256DwGeom.bn &&
-                                 Cfg::BK == kDma256DwGeom.bk && Cfg::STAGES == kDma256DwGeom.stages &&
-                                 Cfg::THREADS == kDma256DwGeom.threads && Cfg::GROUP_M == kDma256DwGeom.group_m &&
-                                 Cfg::C_STAGE_BYTES == kDma256DwGeom.c_stage;
-static_assert(dw_geom_matches<DmaTile256B4> && dw_geom_matches<DmaTile256AB4>,
-              "host geometry of the 4-byte-lane 256 instances out of date");
-static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
-                  dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
-                  dma_geom_matches<DmaTile128T, kDma128> &&
-                  dma_geom_matches<DmaTile64T, kDma64> && dma_geom_matches<DmaTile64x256, kDma64x256> &&
-                  dma_geom_matches<DmaTile64x256T, kDma64x256> && dma_geom_matches<DmaTile256x128W, kDma256x128W> &&
-                  dma_geom_matches<DmaTile256x128WT, kDma256x128W> && dma_geom_matches<DmaTile32W, kDma32W> &&
-                  dma_geom_matches<DmaTile32WT, kDma32W> && dma_geom_matches<DmaTile64W, kDma64W> &&
-                  dma_geom_matches<DmaTile64WT, kDma64W> && dma_geom_matches<DmaTile128W, kDma128W> &&
-                  dma_geom_matches<DmaTile128WT, kDma128W>,
-              "host DMA tile geometry out of date");
-
-template <class Cfg>
-void fill_row(const void** row)
-{
-    row[0] = (const void*)&gemm_relu_tiled<Cfg, kF16, 8, 8>;
-    row[1] = (const void*)&gemm_relu_tiled<Cfg, kF16, 4, 8>;
-    row[2] = (const void*)&gemm_relu_tiled<Cfg, kF16, 8, 4>;
-    row[3] = (const void*)&gemm_relu_tiled<Cfg, kF16, 4, 4>;
-    row[4] = (const void*)&gemm_relu_tiled<Cfg, kF16, 2, 2>;
-    row[5] = (const void*)&gemm_relu_tiled<Cfg, kF16, 1, 1>;
-}
-
-template <class KN, class NK>
-void fill_splitk(DtypeKernels& t, int id)
-{
-    t.splitk[0][id][0] = (const void*)&gemm_relu_dma<KN, kF16, false, true>;
-    t.splitk[0][id][1] = (const void*)&gemm_relu_dma<KN, kF16, true, true>;
-    t.splitk[1][id][0] = (const void*)&gemm_relu_dma<NK, kF16, false, true>;
-    t.splitk[1][id][1] = (const void*)&gemm_relu_dma<NK, kF16, true, true>;
-}
-
-DtypeKernels make_table()
-{
-    DtypeKernels t{};
-    fill_row<Tile256>(t.tiled[kTile256]);
-    fill_row<Tile128>(t.tiled[kTile128]);
-    t.direct = (const void*)&gemm_relu_direct<kF16>;
-    t.dma[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256, kF16, false>;
-    t.dma[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256, kF16, true>;
-    t.dma[kDma128][0] = (const void*)&gemm_relu_dma<DmaTile128, kF16, false>;
-    t.dma[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128, kF16, true>;
-    t.dma[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64, kF16, false>;
-    t.dma[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64, kF16, true>;
-    t.dma256_b4[0][0] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, 0>;
-    t.dma256_b4[0][1] = (const void*)&gemm_relu_dma<DmaTile256B4, kF16, 1>;
-    t.dma256_b4[1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, 0>;
-    t.dma256_b4[1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, kF16, 1>;
-    t.dma256_kfix = (const void*)&gemm_relu_dma<DmaTile256, kF16, 2>;
-    t.direct_nt = (const void*)&gemm_relu_direct<kF16, true>;
-    t.dma_nt[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256T, kF16, false>;
-    t.dma_nt[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256T, kF16, true>;
-    t.dma_nt[kDma128][0] = (const void*)&gemm_relu_dma<DmaTile128T, kF16, false>;
-    t.dma_nt[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128T, kF16, true>;
-    t.dma_nt[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64T, kF16, false>;
-    t.dma_nt[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64T, kF16, true>;
-    t.dma_nt_kfix = (const void*)&gemm_relu_dma<DmaTile256T, kF16, 2>;
-    t.dma[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256, kF16, false>;
-    t.dma[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256, kF16, true>;
-    t.dma_nt[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256T, kF16, false>;
-    t.dma_nt[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256T, kF16, true>;
-    t.dma[kDma256x128W][0] = (const void*)&gemm_relu_dma<DmaTile256x128W, kF16, false>;
-    t.dma[kDma256x128W][1] = (const void*)&gemm_relu_dma<DmaTile256x128W, kF16, true>;
-    t.dma_nt[kDma256x128W][0] = (const void*)&gemm_relu_dma<DmaTile256x128WT, kF16, false>;
-    t.dma_nt[kDma256x128W][1] = (const void*)&gemm_relu_dma<DmaTile256x128WT, kF16, true>;
-    t.dma[kDma32W][0] = (const void*)&gemm_relu_dma<DmaTile32W, kF16, 0>;
-    t.dma[kDma32W][1] = (const void*)&gemm_relu_dma<DmaTile32W, kF16, 1>;
-    t.dma_nt[kDma32W][0] = (const void*)&gemm_relu_dma<DmaTile32WT, kF16, 0>;
-    t.dma_nt[kDma32W][1] = (const void*)&gemm_relu_dma<DmaTile32WT, kF16, 1>;
-    t.dma[kDma64W][0] = (const void*)&gemm_relu_dma<DmaTile64W, kF16, 0>;
-    t.dma[kDma64W][1] = (const void*)&gemm_relu_dma<DmaTile64W, kF16, 1>;
-    t.dma_nt[kDma64W][0] = (const void*)&gemm_relu_dma<DmaTile64WT, kF16, 0>;
-    t.dma_nt[kDma64W][1] = (const void*)&gemm_relu_dma<DmaTile64WT, kF16, 1>;
-    t.dma[kDma128W][0] = (const void*)&gemm_relu_dma<DmaTile128W, kF16, 0>;
-    t.dma[kDma128W][1] = (const void*)&gemm_relu_dma<DmaTile128W, kF16, 1>;
-    t.dma_nt[kDma128W][0] = (const void*)&gemm_relu_dma<DmaTile128WT, kF16, 0>;
-    t.dma_nt[kDma128W][1] = (const void*)&gemm_relu_dma<DmaTile128WT, kF16, 1>;
-    fill_splitk<DmaTile128, DmaTile128T>(t, kDma128);
-    fill_splitk<DmaTile64, DmaTile64T>(t, kDma64);
-    fill_splitk<DmaTile64x256, DmaTile64x256T>(t, kDma64x256);
-    return t;
-}
-}  // namespace
-
 const DtypeKernels& kernels_f16()
 {
-    static const DtypeKernels table = make_table();
+    static const DtypeKernels table = instances::make_table<kF16>();
     return table;
 }
 
