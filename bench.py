@@ -60,11 +60,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make_sets(w, n_sets, device, b_layout=binding.B_KN):
+def make_sets(w, n_sets, device, b_layout=binding.B_KN, data="normal"):
     sets = []
     for i in range(n_sets):
-        g_seed = w.seed + 1000 * i
-        a, b = inputs.normal_pair(w.M, w.N, w.K, w.torch_dtype, w.scale, g_seed)
+        if data == "integer":
+            a, b = inputs.integer_pair(w.M, w.N, w.K, w.torch_dtype, w.int_seed + 1000 * i)
+        else:
+            a, b = inputs.normal_pair(w.M, w.N, w.K, w.torch_dtype, w.scale, w.seed + 1000 * i)
         if b_layout == binding.B_NK:
             b = b.t().contiguous()          # handed over as B^T, (N, K)
         c = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=device)
@@ -156,7 +158,7 @@ def sample_clocks(launch, seconds, interval=0.02):
 
 
 def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN,
-                  splits=None, repeats=1, per_launch_pass=False, clock_seconds=0.0):
+                  splits=None, repeats=1, per_launch_pass=False, clock_seconds=0.0, data="normal"):
     """Time one workload.  After `warmup` untimed launches, `repeats` timed regions of exactly
     `steps` back-to-back launches each, every region bracketed by a device synchronisation and a
     pair of GPU events on the launch stream.  Returns a dict with the median region's ms per step
@@ -164,8 +166,9 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     optionally the mean ms per launch of a pass with a pair of events around every launch, and,
     with clock_seconds > 0, clocks sampled while the workload runs on for that long (outside the
     timed regions).  splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with
-    that many parts."""
-    sets = make_sets(w, n_sets, device, b_layout)
+    that many parts.  data: "normal" (the workload's N(0, 1) * scale inputs) or "integer" (its
+    integer-valued variant)."""
+    sets = make_sets(w, n_sets, device, b_layout, data)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
     lib = gr.load_library()
@@ -196,9 +199,10 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     # Timed regions: K back-to-back launches between two events, nothing else on the stream.
     # In the kernel trace they follow each other with no gap and no overlap, so a region's
     # length over K is both the time per step and each launch's average duration.
-    before = read_clocks()
-    region_ms = []
-    for _ in range(repeats):
+    # The clocks are read from the host while the first and the last region run on the GPU
+    # (after their launches are queued, before the synchronisation that ends them).
+    region_ms, before, after = [], None, None
+    for r in range(repeats):
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize(device)
@@ -206,11 +210,14 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
         for i in range(steps):
             launch(i)
         t1.record(stream)
+        if r == 0:
+            before = read_clocks()
+        if r == repeats - 1:
+            after = read_clocks()
         torch.cuda.synchronize(device)
         region_ms.append(t0.elapsed_time(t1) / steps)
-    after = read_clocks()
     out = {"ms_per_step": sorted(region_ms)[len(region_ms) // 2], "region_ms_per_step": region_ms,
-           "clocks_before": before, "clocks_after": after}
+           "clocks_first_region": before, "clocks_last_region": after}
     if per_launch_pass:
         # The same K launches once more, each between its own pair of events on the launch
         # stream.  The event records add host time to every launch and leave about 10 us
@@ -228,10 +235,10 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     return out
 
 
-def cpu_baseline(w, target_s):
+def cpu_baseline(w, target_s, data="normal"):
     """The CPU oracle on a bounded sample of the workload: whole rows of C."""
     import oracle
-    a, b = inputs.workload_inputs(w)
+    a, b = inputs.workload_inputs(w, data == "integer")
     threads = len(os.sched_getaffinity(0))
     # Grow the row count until one run takes at least half the target time
     # (the first runs are short; only the last, longest run is reported).
@@ -251,13 +258,17 @@ def cpu_baseline(w, target_s):
             "seconds": dt}, ref_rows
 
 
-def parity_rows(w, ref_rows, device, b_layout):
-    """The GPU's C for the workload's seeded inputs (the oracle's), compared with the oracle's
-    rows from the CPU baseline: errors and the tolerance the tests use."""
-    a, b = inputs.workload_inputs(w)
+def parity_rows(w, ref_rows, device, b_layout, config=binding.CONFIG_AUTO, splits=None, data="normal"):
+    """The GPU's C for the workload's seeded inputs (the oracle's), through the entry point and
+    kernel the bench timed, compared with the oracle's rows from the CPU baseline: errors and the
+    tolerance the tests use."""
+    a, b = inputs.workload_inputs(w, data == "integer")
     if b_layout == binding.B_NK:
         b = b.t().contiguous()
-    c = binding.gemm_relu_ex(a.to(device), b.to(device), b_layout=b_layout)
+    if splits is None:
+        c = binding.gemm_relu_ex(a.to(device), b.to(device), b_layout=b_layout, config=config)
+    else:
+        c = binding.gemm_relu_splitk(a.to(device), b.to(device), b_layout=b_layout, config=config, splits=splits)
     torch.cuda.synchronize(device)
     rows = ref_rows.shape[0]
     got_bits = c[:rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -325,6 +336,11 @@ def main():
     p.add_argument("--config", type=int, default=binding.CONFIG_AUTO)
     p.add_argument("--b-layout", choices=["kn", "nk"], default="kn",
                    help="B handed over as (K, N) or as B^T, (N, K)")
+    p.add_argument("--splits", type=int, default=None,
+                   help="time the split-K entry point with this many parts (0: the library chooses) "
+                        "instead of gemm_relu")
+    p.add_argument("--data", choices=["normal", "integer"], default="normal",
+                   help="the workload's N(0, 1) * scale inputs, or its integer-valued variant")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
@@ -354,11 +370,15 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     b_layout = binding.B_NK if args.b_layout == "nk" else binding.B_KN
-    cfg = gr.selected_config(w.M, w.N, w.K, binding.F16 if w.dtype == "fp16" else binding.BF16, args.config,
-                             b_layout=b_layout)
+    dt = binding.F16 if w.dtype == "fp16" else binding.BF16
+    if args.splits is None:
+        cfg = gr.selected_config(w.M, w.N, w.K, dt, args.config, b_layout=b_layout)
+    else:
+        cfg = gr.selected_splitk_config(w.M, w.N, w.K, dt, args.config, args.splits, b_layout=b_layout)
     log(f"[bench] {w.name}: config {cfg}")
     head = time_workload(w, args.steps, args.warmup, args.sets, device, args.config, b_layout,
-                         repeats=args.repeats, clock_seconds=args.clock_seconds)
+                         splits=args.splits, repeats=args.repeats, clock_seconds=args.clock_seconds,
+                         data=args.data)
     ms_step = head["ms_per_step"]
     # One launch per step, back to back with no gap: the step time is the kernel's
     # average launch duration over the timed region.
@@ -366,7 +386,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     log(f"[bench] {w.name}: median {ms_step:.4f} ms/step over {args.repeats} regions "
         f"{[round(x, 4) for x in head['region_ms_per_step']]}, {tflops:.1f} TFLOP/s; "
-        f"clocks before {head['clocks_before']}, after {head['clocks_after']}")
+        f"clocks in the first region {head['clocks_first_region']}, in the last {head['clocks_last_region']}")
     log(f"[bench] clocks under sustained load: {head.get('clocks_sustained')}")
 
     secondary = {}
@@ -380,12 +400,13 @@ def main():
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_DMA_64x256, 4),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
+                ("square_2048", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("square_8192", binding.B_NK, binding.CONFIG_AUTO, None),
                 ("square_8192_bf16", binding.B_KN, binding.CONFIG_AUTO, None)]
         for name, s_layout, s_config, s_splits in runs:
             sw = inputs.WORKLOADS[name]
-            if (sw.name == w.name and s_splits is None and s_config == binding.CONFIG_AUTO and
-                    args.b_layout == ("nk" if s_layout == binding.B_NK else "kn")):
+            if (sw.name == w.name and s_splits == args.splits and s_config == args.config and
+                    args.b_layout == ("nk" if s_layout == binding.B_NK else "kn") and args.data == "normal"):
                 continue
             r = time_workload(sw, 50 if sw.flop < 1e12 else 20, 50, 3, device, config=s_config,
                               b_layout=s_layout, splits=s_splits, repeats=3, per_launch_pass=True)
@@ -403,7 +424,7 @@ def main():
                      "TFLOP/s": round(sw.flop / (s_ms * 1e-3) / 1e12, 2),
                      "frac_mfma_peak": round(sw.flop / (s_ms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_ms * 1e-3) / 1e9, 1),
-                     "sclk_mhz_after": r["clocks_after"]["sclk_mhz"]}
+                     "sclk_mhz_last_region": r["clocks_last_region"]["sclk_mhz"]}
             entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
             secondary[name] = entry
             log(f"[bench] {name}: {entry}")
@@ -411,10 +432,10 @@ def main():
     cpu = parity = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu, ref_rows = cpu_baseline(w, args.cpu_seconds)
+        cpu, ref_rows = cpu_baseline(w, args.cpu_seconds, args.data)
         log(f"[bench] CPU oracle: {cpu}")
         cpu.pop("seconds", None)
-        parity = parity_rows(w, ref_rows, device, b_layout)
+        parity = parity_rows(w, ref_rows, device, b_layout, args.config, args.splits, args.data)
         log(f"[bench] GPU against the oracle's rows: {parity}")
         cpu["small_workloads"] = cpu_small()
         log(f"[bench] CPU oracle, small whole workloads: {cpu['small_workloads']}")
@@ -435,7 +456,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "accumulate": "fp32",
-                   "input_dist": f"N(0,1)*{w.scale}", "kernel": binding.CONFIG_NAMES.get(cfg["config_id"]),
+                   "input_dist": f"N(0,1)*{w.scale}" if args.data == "normal" else "integers uniform in [-2, 2]",
+                   "kernel": binding.CONFIG_NAMES.get(cfg["config_id"]), "splits": cfg["splits"],
                    "block": [cfg["block_m"], cfg["block_n"], cfg["block_k"]], "stages": cfg["stages"],
                    "grid": cfg["grid"], "rotated_sets": args.sets, "b_layout": args.b_layout},
         "frac_of_peak": round(tflops / peak, 4),
@@ -446,8 +468,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "kernel_source_sha256": kernel_source_digest(),
-        "clocks": {"before_timed_regions": head["clocks_before"], "after_timed_regions": head["clocks_after"],
-                   "sustained": head.get("clocks_sustained")},
+        "clocks": {"first_timed_region": head["clocks_first_region"],
+                   "last_timed_region": head["clocks_last_region"], "sustained": head.get("clocks_sustained")},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

@@ -52,7 +52,7 @@ def test_bench_prints_the_contract_line():
     # the median of the timed regions, each of exactly `steps` launches
     assert j["repeats"] == 3 and len(j["region_ms_per_step"]) == 3
     assert j["ms_per_step"] == sorted(j["region_ms_per_step"])[1]
-    for side in ("before_timed_regions", "after_timed_regions"):
+    for side in ("first_timed_region", "last_timed_region"):
         assert set(j["clocks"][side]) == {"sclk_mhz", "mclk_mhz", "power_w"}
 
 

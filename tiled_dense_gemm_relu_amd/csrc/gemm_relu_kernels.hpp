@@ -96,13 +96,15 @@ __device__ __forceinline__ uint16_t relu_cast(float x)
 //  2. Panels: logical ids walk GROUP_M tile-rows at a time, column by column
 //     inside the panel, so the tiles in flight reuse the same few A row-panels
 //     and B column-panels.
+//  xcd_remap = false skips step 1 (the ablation of the remap; results are the
+//  same, only which L2 serves which tiles changes).
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int group_m,
-                                            int& tm, int& tn)
+                                            int& tm, int& tn, bool xcd_remap = true)
 {
     const int total = tiles_m * tiles_n;
     const int per_xcd = total / 8;
     int pid = wg;
-    if (wg < per_xcd * 8) pid = (wg % 8) * per_xcd + wg / 8;
+    if (xcd_remap && wg < per_xcd * 8) pid = (wg % 8) * per_xcd + wg / 8;
     const int panel = group_m * tiles_n;
     const int first_m = (pid / panel) * group_m;
     const int rows = min(tiles_m - first_m, group_m);
@@ -540,11 +542,13 @@ __device__ __forceinline__ int b_swizzle(int k)
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_,
           int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16, bool B_KMAJOR_ = false, int PRODUCERS_ = 0,
-          bool SWIZZLE_ = true>
+          bool SWIZZLE_ = true, bool XCD_REMAP_ = true>
 struct DmaConfig {
     // SWIZZLE = false stores every LDS row unpermuted (the ablation of the XOR
     // swizzle; results are the same, only the bank conflicts differ).
-    static constexpr bool SWIZZLE = SWIZZLE_;
+    // XCD_REMAP = false maps tiles to workgroups without the XCD remap (the
+    // ablation of the remap; results are the same).
+    static constexpr bool SWIZZLE = SWIZZLE_, XCD_REMAP = XCD_REMAP_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, GROUP_M = GROUP_M_;
     // WAVES compute waves; PRODUCERS > 0 adds that many waves that only issue
     // the LDS DMA (wave specialisation), else every compute wave loads its share.
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     }
     auto tile_origin = [&](int tile, int& m0, int& n0) {
         int tm, tn;
-        tile_coords(tile, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);
+        tile_coords(tile, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn, Cfg::XCD_REMAP);
         m0 = tm * BM;
         n0 = tn * BN;
     };

@@ -1,21 +1,33 @@
-// Layout ablation: the 256x256x64 LDS-DMA kernel with and without the XOR
-// swizzle of its LDS rows, on ReLU(A @ B) 8192^3 fp16 (entries N(0, 0.1^2)).
+// Layout ablations of the 256x256x64 LDS-DMA kernel on ReLU(A @ B) 8192^3 fp16
+// (entries N(0, 0.1^2)):
+//   product     the library's kernel: XOR-swizzled LDS rows, XCD-aware remap
+//   unswizzled  LDS rows stored unpermuted
+//   no_remap    tiles handed to workgroups without the XCD remap (the panel
+//               order of GROUP_M tile-rows is kept)
 //
 // The pages report that swizzling the shared-memory layout cut the share of
 // kernel time spent in shared-memory reads from 41% to 17% (the zwxr.cn
-// hands-on TileLang article, section 2.3, hardware not stated).  This program
-// measures the same switch on gfx950: both variants run in one process,
-// alternating, and must give bit-identical C.  Run it under
-//   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE ... -- ./layout_ablation
-// for the bank-conflict counters of each variant (the kernels differ in their
-// DmaConfig's last template argument).
+// hands-on TileLang article, section 2.3, hardware not stated), and that
+// threadblock rasterization (T.use_swizzle with a panel size) gains a few
+// percent of bandwidth ("Writing High-Performance Kernels in TileLang",
+// section "Let's write a GEMM").  This program measures both switches on
+// gfx950: the variants run in one process, alternating, and must give
+// bit-identical C.  Run one variant under
+//   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE ... -- ./layout_ablation --variant unswizzled
+// for its counters.
 //
+// Usage: layout_ablation [--variant all|product|unswizzled|no_remap] [--rounds R] [--reps N] [--zero]
+// --zero: A = B = 0 instead of normal entries.  Bank conflicts and cache traffic
+// do not depend on the values, and zeros keep the shader clock at its maximum
+// (normal fp16 data drives this workload to the board's power cap), so they
+// show each variant's cycles at full clock and start in a fraction of a second.
 // Output: one JSON line per round, then {"outputs_identical": ...}.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <random>
 #include <string>
 #include <vector>
@@ -25,8 +37,9 @@
 namespace {
 
 using namespace gemm_relu_hip;
-using Swizzled = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true>;
-using Plain = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, false>;
+using Product = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true, true>;
+using Unswizzled = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, false, true>;
+using NoRemap = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true, false>;
 
 #define CHECK(x)                                                                               \
     do {                                                                                       \
@@ -64,9 +77,38 @@ float time_kernel(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int 
 
 }  // namespace
 
-int main()
+int main(int argc, char** argv)
 {
-    const int M = 8192, N = 8192, K = 8192, rounds = 4, reps = 30;
+    std::string variant = "all";
+    int rounds = 4, reps = 30;
+    bool zero = false;
+    for (int i = 1; i < argc; ++i) {
+        if (!std::strcmp(argv[i], "--zero")) {
+            zero = true;
+            continue;
+        }
+        if (i + 1 >= argc) {
+            std::fprintf(stderr, "option %s needs a value\n", argv[i]);
+            return 2;
+        }
+        if (!std::strcmp(argv[i], "--variant")) variant = argv[++i];
+        else if (!std::strcmp(argv[i], "--rounds")) rounds = std::atoi(argv[++i]);
+        else if (!std::strcmp(argv[i], "--reps")) reps = std::atoi(argv[++i]);
+        else {
+            std::fprintf(stderr, "unknown option %s\n", argv[i]);
+            return 2;
+        }
+    }
+    const bool all = variant == "all";
+    if (!all && variant != "product" && variant != "unswizzled" && variant != "no_remap") {
+        std::fprintf(stderr, "unknown variant %s\n", variant.c_str());
+        return 2;
+    }
+    if (rounds < 1 || rounds > 100 || reps < 1 || reps > 1000) {
+        std::fprintf(stderr, "rounds in 1..100 and reps in 1..1000\n");
+        return 2;
+    }
+    const int M = 8192, N = 8192, K = 8192;
     int dev = 0;
     hipDeviceProp_t prop;
     CHECK(hipGetDevice(&dev));
@@ -75,38 +117,63 @@ int main()
         std::fprintf(stderr, "needs a gfx950 GPU, found %s\n", prop.gcnArchName);
         return 2;
     }
-    // Row-major A (M x K) and B (K x N), fp16 N(0, 0.1^2); the shapes match the
-    // kernel's tiles exactly, so no tail instance is needed.
-    std::vector<_Float16> host((size_t)M * K);
-    std::mt19937 rng(1003);
-    std::normal_distribution<float> normal(0.0f, 0.1f);
-    uint16_t *A = nullptr, *B = nullptr, *C1 = nullptr, *C2 = nullptr;
+    // Row-major A (M x K) and B (K x N), fp16 N(0, 0.1^2) (or zeros); the shapes
+    // match the kernel's tiles exactly, so no tail instance is needed.
+    uint16_t *A = nullptr, *B = nullptr;
+    uint16_t* C[3] = {nullptr, nullptr, nullptr};
     CHECK(hipMalloc(&A, (size_t)M * K * 2));
     CHECK(hipMalloc(&B, (size_t)K * N * 2));
-    CHECK(hipMalloc(&C1, (size_t)M * N * 2));
-    CHECK(hipMalloc(&C2, (size_t)M * N * 2));
-    for (auto& x : host) x = (_Float16)normal(rng);
-    CHECK(hipMemcpy(A, host.data(), host.size() * 2, hipMemcpyHostToDevice));
-    for (auto& x : host) x = (_Float16)normal(rng);
-    CHECK(hipMemcpy(B, host.data(), host.size() * 2, hipMemcpyHostToDevice));
+    for (auto& c : C) CHECK(hipMalloc(&c, (size_t)M * N * 2));
+    if (zero) {
+        CHECK(hipMemset(A, 0, (size_t)M * K * 2));
+        CHECK(hipMemset(B, 0, (size_t)K * N * 2));
+    } else {
+        std::vector<_Float16> host((size_t)M * K);
+        std::mt19937 rng(1003);
+        std::normal_distribution<float> normal(0.0f, 0.1f);
+        for (auto& x : host) x = (_Float16)normal(rng);
+        CHECK(hipMemcpy(A, host.data(), host.size() * 2, hipMemcpyHostToDevice));
+        for (auto& x : host) x = (_Float16)normal(rng);
+        CHECK(hipMemcpy(B, host.data(), host.size() * 2, hipMemcpyHostToDevice));
+    }
 
     const double flop = 2.0 * M * N * K;
+    const int cus = prop.multiProcessorCount;
+    bool ran[3] = {false, false, false};
     for (int r = 0; r < rounds; ++r) {
-        const float ts = time_kernel<Swizzled>(A, B, C1, M, N, K, prop.multiProcessorCount, reps);
-        const float tp = time_kernel<Plain>(A, B, C2, M, N, K, prop.multiProcessorCount, reps);
-        std::printf("{\"round\": %d, \"swizzled_ms\": %.4f, \"swizzled_tflops\": %.1f, \"unswizzled_ms\": %.4f, "
-                    "\"unswizzled_tflops\": %.1f}\n",
-                    r, ts, flop / ts / 1e9, tp, flop / tp / 1e9);
+        std::string line = "{\"round\": " + std::to_string(r);
+        auto report = [&](const char* name, float ms) {
+            char buf[160];
+            std::snprintf(buf, sizeof buf, ", \"%s_ms\": %.4f, \"%s_tflops\": %.1f", name, ms, name, flop / ms / 1e9);
+            line += buf;
+        };
+        if (all || variant == "product") {
+            report("product", time_kernel<Product>(A, B, C[0], M, N, K, cus, reps));
+            ran[0] = true;
+        }
+        if (all || variant == "unswizzled") {
+            report("unswizzled", time_kernel<Unswizzled>(A, B, C[1], M, N, K, cus, reps));
+            ran[1] = true;
+        }
+        if (all || variant == "no_remap") {
+            report("no_remap", time_kernel<NoRemap>(A, B, C[2], M, N, K, cus, reps));
+            ran[2] = true;
+        }
+        std::printf("%s}\n", line.c_str());
         std::fflush(stdout);
     }
-    std::vector<uint16_t> c1((size_t)M * N), c2((size_t)M * N);
-    CHECK(hipMemcpy(c1.data(), C1, c1.size() * 2, hipMemcpyDeviceToHost));
-    CHECK(hipMemcpy(c2.data(), C2, c2.size() * 2, hipMemcpyDeviceToHost));
-    const bool same = c1 == c2;
+    // Every variant that ran must give the same C bit for bit.
+    std::vector<uint16_t> first, other((size_t)M * N);
+    bool same = true;
+    for (int v = 0; v < 3; ++v) {
+        if (!ran[v]) continue;
+        CHECK(hipMemcpy(other.data(), C[v], other.size() * 2, hipMemcpyDeviceToHost));
+        if (first.empty()) first = other;
+        else same = same && first == other;
+    }
     std::printf("{\"outputs_identical\": %s}\n", same ? "true" : "false");
     CHECK(hipFree(A));
     CHECK(hipFree(B));
-    CHECK(hipFree(C1));
-    CHECK(hipFree(C2));
+    for (auto& c : C) CHECK(hipFree(c));
     return same ? 0 : 1;
 }

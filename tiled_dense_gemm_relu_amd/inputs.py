@@ -53,7 +53,7 @@ class Workload:
 # The workload shapes: a small correctness case, the 1024^3 example shape with
 # 128x128x64 tiles, the 8192^3 compute-bound headline, a shape with ragged M, N
 # and K tails, a skinny decode-like bf16 shape that is HBM-bound, a deep-K
-# shape with few output tiles, and the headline shape in bf16.
+# shape with few output tiles, the headline shape in bf16 and a mid-size square.
 WORKLOADS = {
     "small_256": Workload("small_256", 256, 256, 256, "fp16", 1.0, 1001, 1011),
     "square_1024": Workload("square_1024", 1024, 1024, 1024, "fp16", 1.0, 1002, 1012),
@@ -66,6 +66,8 @@ WORKLOADS = {
     "deep_512x512x16384": Workload("deep_512x512x16384", 512, 512, 16384, "fp16", 0.05, 1006, 1016),
     # the headline shape in bf16
     "square_8192_bf16": Workload("square_8192_bf16", 8192, 8192, 8192, "bf16", 0.1, 1007, 1017),
+    # a mid-size square: 128x128 tiles fill the CUs, 256x256 ones do not
+    "square_2048": Workload("square_2048", 2048, 2048, 2048, "fp16", 0.1, 1008, 1018),
 }
 
 
