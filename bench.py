@@ -65,6 +65,9 @@ def make_sets(w, n_sets, device, b_layout=binding.B_KN, data="normal"):
     for i in range(n_sets):
         if data == "integer":
             a, b = inputs.integer_pair(w.M, w.N, w.K, w.torch_dtype, w.int_seed + 1000 * i)
+        elif data == "zero":
+            a = torch.zeros((w.M, w.K), dtype=w.torch_dtype)
+            b = torch.zeros((w.K, w.N), dtype=w.torch_dtype)
         else:
             a, b = inputs.normal_pair(w.M, w.N, w.K, w.torch_dtype, w.scale, w.seed + 1000 * i)
         if b_layout == binding.B_NK:
@@ -123,6 +126,33 @@ def read_clocks():
     return out
 
 
+def read_power_cap():
+    """The board's package power limit in W (hwmon power1_cap), or "unavailable"."""
+    import glob
+    global _SYSFS
+    if _SYSFS is None:
+        _SYSFS = _gpu_sysfs_dir() or ""
+    for f in sorted(glob.glob(os.path.join(_SYSFS, "hwmon", "hwmon*", "power1_cap"))) if _SYSFS else []:
+        try:
+            return round(int(open(f).read().strip()) / 1e6, 1)
+        except (OSError, ValueError):
+            continue
+    return "unavailable"
+
+
+def power_clock_context(tflops, peak, sustained):
+    """The throughput against the MFMA peak at the shader clock the board sustained on this workload
+    (peak x sclk / 2400 MHz), beside the package power and its cap: on normal fp16 data the board
+    lowers the clock to hold its power limit."""
+    if not sustained or isinstance(sustained.get("sclk_mhz"), str):
+        return {"sustained_sclk_mhz": "unavailable", "power_cap_w": read_power_cap()}
+    sclk = sustained["sclk_mhz"]["median"]
+    pw = sustained["power_w"]
+    return {"sustained_sclk_mhz": sclk, "peak_at_sustained_sclk": round(peak * sclk / 2400.0, 1),
+            "frac_of_peak_at_sustained_sclk": round(tflops / (peak * sclk / 2400.0), 4),
+            "sustained_power_w": pw["median"] if isinstance(pw, dict) else pw, "power_cap_w": read_power_cap()}
+
+
 def sample_clocks(launch, seconds, interval=0.02):
     """Keep the GPU busy with `launch` for about `seconds` while the clocks (and power, where the
     board reports it) are read every `interval` s.  Returns medians and ranges over the samples."""
@@ -166,8 +196,8 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     optionally the mean ms per launch of a pass with a pair of events around every launch, and,
     with clock_seconds > 0, clocks sampled while the workload runs on for that long (outside the
     timed regions).  splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with
-    that many parts.  data: "normal" (the workload's N(0, 1) * scale inputs) or "integer" (its
-    integer-valued variant)."""
+    that many parts.  data: "normal" (the workload's N(0, 1) * scale inputs), "integer" (its
+    integer-valued variant) or "zero"."""
     sets = make_sets(w, n_sets, device, b_layout, data)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
@@ -239,6 +269,8 @@ def cpu_baseline(w, target_s, data="normal"):
     """The CPU oracle on a bounded sample of the workload: whole rows of C."""
     import oracle
     a, b = inputs.workload_inputs(w, data == "integer")
+    if data == "zero":
+        a, b = torch.zeros_like(a), torch.zeros_like(b)
     threads = len(os.sched_getaffinity(0))
     # Grow the row count until one run takes at least half the target time
     # (the first runs are short; only the last, longest run is reported).
@@ -263,6 +295,8 @@ def parity_rows(w, ref_rows, device, b_layout, config=binding.CONFIG_AUTO, split
     kernel the bench timed, compared with the oracle's rows from the CPU baseline: errors and the
     tolerance the tests use."""
     a, b = inputs.workload_inputs(w, data == "integer")
+    if data == "zero":
+        a, b = torch.zeros_like(a), torch.zeros_like(b)
     if b_layout == binding.B_NK:
         b = b.t().contiguous()
     if splits is None:
@@ -339,8 +373,9 @@ def main():
     p.add_argument("--splits", type=int, default=None,
                    help="time the split-K entry point with this many parts (0: the library chooses) "
                         "instead of gemm_relu")
-    p.add_argument("--data", choices=["normal", "integer"], default="normal",
-                   help="the workload's N(0, 1) * scale inputs, or its integer-valued variant")
+    p.add_argument("--data", choices=["normal", "integer", "zero"], default="normal",
+                   help="the workload's N(0, 1) * scale inputs, its integer-valued variant, or zeros (the "
+                        "last two draw less power: for clock and power comparisons, not the metric)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
@@ -456,7 +491,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "accumulate": "fp32",
-                   "input_dist": f"N(0,1)*{w.scale}" if args.data == "normal" else "integers uniform in [-2, 2]",
+                   "input_dist": {"normal": f"N(0,1)*{w.scale}", "integer": "integers uniform in [-2, 2]",
+                                  "zero": "zeros"}[args.data],
                    "kernel": binding.CONFIG_NAMES.get(cfg["config_id"]), "splits": cfg["splits"],
                    "block": [cfg["block_m"], cfg["block_n"], cfg["block_k"]], "stages": cfg["stages"],
                    "grid": cfg["grid"], "rotated_sets": args.sets, "b_layout": args.b_layout},
@@ -470,6 +506,7 @@ def main():
         "kernel_source_sha256": kernel_source_digest(),
         "clocks": {"first_timed_region": head["clocks_first_region"],
                    "last_timed_region": head["clocks_last_region"], "sustained": head.get("clocks_sustained")},
+        "power_clock": power_clock_context(tflops, peak, head.get("clocks_sustained")),
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
