@@ -1,7 +1,8 @@
 """Launch-bound callers capture the library's calls in HIP graphs: the entry
 points issue only kernel launches on the caller's stream (no allocation, no
-memset), and split-K's counters return to zero after every call, so a captured
-call can be replayed.  Each replay is checked against the oracle, with new
+memset), and split-K's counters return to zero after every call (the
+no-allocation variant clears its own with a fill kernel), so a captured call
+can be replayed.  Each replay is checked against the oracle, with new
 inputs copied in between replays."""
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ from test_gpu_parity import bits
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kind", ["plain", "b_nk", "splitk"])
+@pytest.mark.parametrize("kind", ["plain", "b_nk", "splitk", "splitk_noalloc"])
 def test_graph_replays_match_the_oracle(kind):
     M, N, K = 192, 320, 512
     dev = torch.device("cuda:0")
@@ -31,8 +32,11 @@ def test_graph_replays_match_the_oracle(kind):
             gr.gemm_relu(a, b, out=c)
         elif kind == "b_nk":
             gr.gemm_relu_ex(a, b, out=c, b_layout=gr.B_NK)
-        else:
+        elif kind == "splitk":
             gr.gemm_relu_splitk(a, b, out=c, splits=4, workspace=ws)
+        else:
+            # the static scratch: its counters are cleared by a fill kernel inside the graph
+            gr.gemm_relu_splitk_noalloc(a, b, out=c, splits=4)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
