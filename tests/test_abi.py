@@ -361,8 +361,15 @@ def test_noalloc_rejects_calls_beyond_its_scratch(lib):
     # the header's size is the binding's
     text = open(HEADER).read()
     assert "#define GEMM_RELU_NOALLOC_SCRATCH_BYTES ((int64_t)65536 + ((int64_t)32 << 20))" in text
-    # every shape the library splits by itself fits (at most ~256 units of partial tiles)
-    for shape in [(64, 16384, 8192, 1), (512, 512, 16384, 0), (1024, 1024, 1024, 0), (2000, 1500, 4096, 0)]:
-        M, N, K, dt = shape
-        cfg = gr.selected_splitk_config(M, N, K, dtype=dt)
-        assert cfg["workspace_bytes"] <= binding.NOALLOC_SCRATCH_BYTES, shape
+    # every split the library chooses by itself fits: fewer than 192 tiles, parts for about 256
+    # units, so at most 447 partial tiles of at most 64 KiB
+    sizes = [64, 128, 192, 256, 320, 512, 640, 1024, 1536, 1792, 2048, 2304]
+    split_seen = 0
+    for M in sizes:
+        for N in sizes + [16384]:
+            for dt in (0, 1):
+                for layout in (gr.B_KN, gr.B_NK):
+                    cfg = gr.selected_splitk_config(M, N, 4096, dtype=dt, b_layout=layout)
+                    assert cfg["workspace_bytes"] <= binding.NOALLOC_SCRATCH_BYTES, (M, N, dt, layout, cfg)
+                    split_seen += cfg["splits"] > 1
+    assert split_seen > 50
