@@ -132,7 +132,9 @@ def read_power_cap():
     global _SYSFS
     if _SYSFS is None:
         _SYSFS = _gpu_sysfs_dir() or ""
-    for f in sorted(glob.glob(os.path.join(_SYSFS, "hwmon", "hwmon*", "power1_cap"))) if _SYSFS else []:
+    if not _SYSFS:
+        return "unavailable"
+    for f in sorted(glob.glob(os.path.join(_SYSFS, "hwmon", "hwmon*", "power1_cap"))):
         try:
             return round(int(open(f).read().strip()) / 1e6, 1)
         except (OSError, ValueError):

@@ -59,3 +59,36 @@ def test_bench_prints_the_contract_line():
 def test_zero_repeats_are_refused():
     res = run("--repeats", "0")
     assert res.returncode == 2
+
+
+def _fake_sysfs(tmp_path, sclk_lines, power_uw, cap_uw):
+    d = tmp_path / "card0" / "device"
+    (d / "hwmon" / "hwmon3").mkdir(parents=True)
+    (d / "vendor").write_text("0x1002\n")
+    (d / "pp_dpm_sclk").write_text(sclk_lines)
+    (d / "pp_dpm_mclk").write_text("0: 2000Mhz *\n")
+    (d / "hwmon" / "hwmon3" / "power1_input").write_text(f"{power_uw}\n")
+    (d / "hwmon" / "hwmon3" / "power1_cap").write_text(f"{cap_uw}\n")
+    return str(d)
+
+
+def test_clock_and_power_readers_parse_the_driver_files(tmp_path, monkeypatch):
+    # The formats the amdgpu driver uses on these boards: the active shader-clock level is marked
+    # with '*' (under load the middle level carries the live frequency, idle shows the sleep level).
+    import bench
+    d = _fake_sysfs(tmp_path, "S: 100Mhz\n0: 500Mhz\n1: 1608Mhz *\n2: 2400Mhz\n", 1353000000, 1400000000)
+    monkeypatch.setattr(bench, "_SYSFS", d)
+    assert bench.read_clocks() == {"sclk_mhz": 1608, "mclk_mhz": 2000, "power_w": 1353.0}
+    assert bench.read_power_cap() == 1400.0
+    ctx = bench.power_clock_context(1254.95, 2500.0, {"sclk_mhz": {"median": 1555}, "power_w": {"median": 1400.0}})
+    assert ctx["peak_at_sustained_sclk"] == round(2500.0 * 1555 / 2400, 1)
+    assert abs(ctx["frac_of_peak_at_sustained_sclk"] - 1254.95 / (2500.0 * 1555 / 2400)) < 1e-4
+    assert (ctx["sustained_power_w"], ctx["power_cap_w"]) == (1400.0, 1400.0)
+
+
+def test_clock_readers_report_unavailable_without_a_gpu(monkeypatch):
+    import bench
+    monkeypatch.setattr(bench, "_SYSFS", "")
+    assert bench.read_clocks() == {"sclk_mhz": "unavailable", "mclk_mhz": "unavailable", "power_w": "unavailable"}
+    assert bench.read_power_cap() == "unavailable"
+    assert bench.power_clock_context(1.0, 2500.0, None)["sustained_sclk_mhz"] == "unavailable"
