@@ -182,13 +182,14 @@ int gemm_relu_selected_config(int64_t M, int64_t N, int64_t K, int dtype, int* b
  * C = ReLU(A @ B) with B stored as `b_layout` says (GEMM_RELU_B_*) and a kernel
  * configuration (GEMM_RELU_CONFIG_*, or GEMM_RELU_CONFIG_AUTO).  With
  * GEMM_RELU_B_KN it is gemm_relu_with_config.  With GEMM_RELU_B_NK, B points
- * to the (N, K) array B^T; only the DMA_* and DIRECT kernels read it: a TILE_256
- * or TILE_128 request is served by DMA_256 or DMA_128, DMA_128 and DMA_64 need
- * K % 8 == 0 with 16-byte aligned A and B (else DMA_256 serves them), DMA_256
- * needs K even with 4-byte aligned A and B (else DIRECT serves it).  Results,
- * limits (B^T's 256-row band must stay below 2^31 bytes), memory, stream and
- * error behaviour are those of gemm_relu; GEMM_RELU_ERR_BAD_LAYOUT for an
- * unknown b_layout.
+ * to the (N, K) array B^T, whose rows are K-contiguous like A's: every kernel
+ * reads it.  The DMA_* kernels other than DMA_256 need K % 8 == 0 with 16-byte
+ * aligned A and B (else DMA_256 serves them); DMA_256 needs K even with 4-byte
+ * aligned A and B (else TILE_256 serves it); TILE_256, TILE_128 and DIRECT
+ * take any K and alignment, with loads along K as wide as K and the pointers
+ * allow.  Results, limits (B^T's 256-row band must stay below 2^31 bytes),
+ * memory, stream and error behaviour are those of gemm_relu;
+ * GEMM_RELU_ERR_BAD_LAYOUT for an unknown b_layout.
  */
 int gemm_relu_ex(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
                  int b_layout, int config_id, void* stream);

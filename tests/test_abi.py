@@ -198,22 +198,28 @@ def test_b_nk_config_choice():
     assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"], cfg["stages"]) == (3, 8, 8, 64, 2)
     cfg = nt_config(8192, 8192, 8192, b_ptr=(1 << 20) + 4)           # B^T only 4-byte aligned
     assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"], cfg["block_k"]) == (3, 8, 8, 64)
-    # odd K, or 2-byte alignment: the direct kernel
-    assert nt_config(1024, 1024, 1031)["config_id"] == 0
-    assert nt_config(8192, 8192, 8192, a_ptr=4096 + 2)["config_id"] == 0
+    # odd K, or 2-byte alignment: the register-staged kernels, which load B^T like A
+    cfg = nt_config(1024, 1024, 1031)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (2, 1, 1)
+    cfg = nt_config(8192, 8192, 8192, a_ptr=4096 + 2)                # (1, 8) has no instance: (1, 1)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (1, 1, 1)
+    cfg = nt_config(8192, 8192, 8190, b_ptr=(1 << 20) + 2)           # B^T rows of an even length, 2-byte aligned
+    assert (cfg["config_id"], cfg["vec_b"]) == (1, 1)
 
 
 def test_b_nk_forced_configs():
-    # the register-staged kernels do not read B^T: TILE_* means the DMA tile of that size
-    assert nt_config(512, 512, 512, config=1)["config_id"] == 3
-    assert nt_config(512, 512, 512, config=2)["config_id"] == 4
+    # the register-staged kernels read B^T too (TILE_* means them in both layouts)
+    assert nt_config(512, 512, 512, config=1)["config_id"] == 1
+    assert nt_config(512, 512, 512, config=2)["config_id"] == 2
     for dma in (3, 4, 5):
         assert nt_config(512, 512, 512, config=dma)["config_id"] == dma
-        assert nt_config(512, 512, 516, config=dma)["config_id"] == 3
-        assert nt_config(512, 512, 515, config=dma)["config_id"] == 0
+        assert nt_config(512, 512, 516, config=dma)["config_id"] == 3      # K even: the 256 DMA tile
+    assert nt_config(512, 512, 515, config=3)["config_id"] == 1             # odd K: register-staged
+    for dma in (4, 5, 8, 9, 10):
+        assert nt_config(512, 512, 515, config=dma)["config_id"] == 2
     assert nt_config(512, 512, 515, config=0)["config_id"] == 0
     cfg = nt_config(512, 512, 516, config=1)
-    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (3, 8, 8)
+    assert (cfg["config_id"], cfg["vec_a"], cfg["vec_b"]) == (1, 4, 4)     # K % 8 == 4: 4-element loads
 
 
 def test_splitk_config_choice():

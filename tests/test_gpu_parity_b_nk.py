@@ -176,3 +176,24 @@ def test_b_nk_wrapper_checks_shapes():
         gr.gemm_relu_ex(a, torch.ones((5, 8), dtype=torch.float16, device="cuda"), b_layout=7)
     assert gr.gemm_relu_ex(a, torch.ones((5, 8), dtype=torch.float16, device="cuda"),
                            b_layout=gr.B_NK).shape == (4, 5)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("shape", [(300, 520, 201), (700, 900, 1031), (4100, 264, 77)])
+def test_b_nk_odd_k_takes_the_register_staged_kernel(shape, dtype):
+    # With odd K, B^T rows are only 2-byte aligned: no LDS-DMA lane width fits, and AUTO takes the
+    # register-staged kernel, which loads B^T like A (elements along K), over several tiles.
+    M, N, K = shape
+    a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=M + 3 * N + 7 * K)
+    want = oracle.gemm_relu(a, b, dtype)
+    code = gr.F16 if dtype == "fp16" else gr.BF16
+    bt = b.t().contiguous().cuda()
+    cfg = gr.selected_config(M, N, K, dtype=code, b_layout=gr.B_NK, a_ptr=1 << 20, b_ptr=1 << 21)
+    assert cfg["config_id"] in (binding.CONFIG_TILE_256, binding.CONFIG_TILE_128) and cfg["vec_b"] == 1
+    for config in (binding.CONFIG_AUTO, binding.CONFIG_TILE_256, binding.CONFIG_TILE_128, binding.CONFIG_DMA_256,
+                   binding.CONFIG_DIRECT):
+        c = gr.gemm_relu_ex(a.cuda(), bt, b_layout=gr.B_NK, config=config)
+        torch.cuda.synchronize()
+        got = bits(c)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (config, f"{len(bad)} differ, first at {tuple(bad[0])}")

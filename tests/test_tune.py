@@ -31,8 +31,9 @@ def test_candidates_are_distinct_resolved_configurations():
         r = gr.selected_splitk_config(512, 512, 16384, config=c, splits=s) if s > 1 else \
             gr.selected_config(512, 512, 16384, config=c)
         assert (r["config_id"], r["splits"]) == (c, s)
-    # odd K: only the kernels that take 2-byte loads remain, the direct kernel among them for B (N, K)
-    assert tune.candidates(100, 100, 101, gr.F16, gr.B_NK) == [(0, 1)]
+    # odd K: only the kernels that take 2-byte loads remain, the register-staged ones in both layouts
+    assert tune.candidates(100, 100, 101, gr.F16, gr.B_NK) == [(1, 1), (2, 1)]
+    assert tune.candidates(100, 100, 101, gr.F16, gr.B_KN) == [(1, 1), (2, 1)]
 
 
 def test_split_candidates_respect_the_workspace_cap():

@@ -180,25 +180,25 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     // for: with producer waves (measured faster at 2048^3).
     const int mid_dma = splits_req > 0 ? GEMM_RELU_CONFIG_DMA_128 : GEMM_RELU_CONFIG_DMA_128x128_WS;
     if (plan->b_nk) {
-        // B as (N, K): only the LDS-DMA kernels (16-byte lanes for both
-        // operands, or 4-byte lanes for both in the 256 one) and the direct
-        // kernel read it.  A TILE_* request means the DMA tile of its size.
+        // B as (N, K): its rows are K-contiguous like A's.  The LDS-DMA kernels
+        // need 16-byte lanes for both operands, or (the 256 one) 4-byte aligned
+        // rows; otherwise (odd K, 2-byte alignment) the register-staged kernels,
+        // which load B^T like A, take it.
         if (chosen == GEMM_RELU_CONFIG_AUTO) {
             const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
             const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
-            if (t256 >= 192 || (!full_vectors && dword_vectors))
+            if (!dword_vectors)
+                chosen = t256 >= 192 ? GEMM_RELU_CONFIG_TILE_256 : GEMM_RELU_CONFIG_TILE_128;
+            else if (t256 >= 192 || !full_vectors)
                 chosen = GEMM_RELU_CONFIG_DMA_256;
             else
                 chosen = t128 >= 192 ? mid_dma : small_dma;
         }
-        if (chosen == GEMM_RELU_CONFIG_TILE_256) chosen = GEMM_RELU_CONFIG_DMA_256;
-        if (chosen == GEMM_RELU_CONFIG_TILE_128) chosen = GEMM_RELU_CONFIG_DMA_128;
         if ((chosen == GEMM_RELU_CONFIG_DMA_128 || chosen == GEMM_RELU_CONFIG_DMA_64 ||
              chosen == GEMM_RELU_CONFIG_DMA_64x256 || chosen == GEMM_RELU_CONFIG_DMA_256x128_WS ||
              chosen == GEMM_RELU_CONFIG_DMA_32x32_WS || chosen == GEMM_RELU_CONFIG_DMA_64x64_WS ||
-             chosen == GEMM_RELU_CONFIG_DMA_128x128_WS) && !full_vectors)
+             chosen == GEMM_RELU_CONFIG_DMA_128x128_WS) && !full_vectors && dword_vectors)
             chosen = GEMM_RELU_CONFIG_DMA_256;
-        if (chosen == GEMM_RELU_CONFIG_DMA_256 && !dword_vectors) chosen = GEMM_RELU_CONFIG_DIRECT;
     }
     if (chosen == GEMM_RELU_CONFIG_AUTO) {
         // The largest tile that still yields enough workgroups to cover the 256
@@ -290,8 +290,10 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
     const int tile = chosen == GEMM_RELU_CONFIG_TILE_256 ? kTile256 : kTile128;
     const TileGeom& g = kTileGeom[tile];
     // Each workgroup addresses A through a descriptor over bm rows and B through
-    // one over bk rows; both must stay below 2^31 bytes.
-    if (int64_t(g.bm) * K * 2 > kMaxBand || int64_t(g.bk) * N * 2 > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
+    // one over bk rows (B stored (N, K): over bn rows of B^T); both must stay
+    // below 2^31 bytes.
+    const int64_t b_band = plan->b_nk ? int64_t(g.bn) * K * 2 : int64_t(g.bk) * N * 2;
+    if (int64_t(g.bm) * K * 2 > kMaxBand || b_band > kMaxBand) return GEMM_RELU_ERR_TOO_LARGE;
     const int64_t tm = ceil_div(M, g.bm), tn = ceil_div(N, g.bn);
     if (tm * tn > INT32_MAX) return GEMM_RELU_ERR_TOO_LARGE;
 
@@ -386,8 +388,8 @@ int launch(const Plan& p, const void* A, const void* B, void* C, int64_t M, int6
     } else if (p.tile >= 0) {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok;
         void* args[] = {&A, &B, &C, &m, &n, &k, &tiles_m, &tiles_n, &c_vec_ok};
-        err = hipLaunchKernel(ks.tiled[p.tile][p.vec_pair], dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads),
-                              args, 0, stream);
+        const void* fn = p.b_nk ? ks.tiled_nt[p.tile][p.vec_pair] : ks.tiled[p.tile][p.vec_pair];
+        err = hipLaunchKernel(fn, dim3((unsigned)p.cfg.grid), dim3((unsigned)p.cfg.threads), args, 0, stream);
     } else {
         int tiles_m = p.tiles_m, tiles_n = p.tiles_n, c_vec_ok = p.c_vec_ok, splits = p.splits;
         int* counters = p.splits > 1 ? static_cast<int*>(workspace) : nullptr;

@@ -276,7 +276,10 @@ struct TileConfig {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <class Cfg, int DT, int VA, int VB>
+// B_NK: B is given as B^T, an (N, K) row-major array.  Its rows are K-contiguous
+// like A's, so its tile is loaded and stored exactly as A's (no transpose), and
+// the fragment reads are unchanged.  VB then counts elements along K.
+template <class Cfg, int DT, int VA, int VB, bool B_NK = false>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int M, int N, int K, int tiles_m, int tiles_n, int c_vec_ok)
@@ -314,9 +317,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
     const int b_kb = tid / (BN / 8);
     const int b_col = n0 + b_nb * 8;
     const uint32_t b_off = (uint32_t)(b_kb * KB) * (uint32_t)N * 2u + (uint32_t)b_col * 2u;
+    // B^T (B_NK): rows n0 .. n0 + valid_n - 1 of the (N, K) array; chunks as A's.
+    constexpr int BT_CHUNKS = BN * (BK / 8) / THREADS;
+    static_assert(!B_NK || BT_CHUNKS * THREADS == BN * (BK / 8), "B^T tile must split evenly over threads");
+    const __amdgpu_buffer_rsrc_t rsrc_bt =
+        make_rsrc(B + (size_t)(B_NK ? n0 : 0) * (size_t)K, B_NK ? (uint32_t)min(BN, N - n0) * (uint32_t)K * 2u : 0u);
 
     u32x4 ra[Cfg::A_CHUNKS];
-    u32x4 rb[KB];
+    u32x4 rb[B_NK ? BT_CHUNKS : KB];
 
     auto global_load = [&](int kt) {
         const int k0 = kt * BK;
@@ -326,13 +334,23 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
             const uint32_t off = (uint32_t)a_row[i] * (uint32_t)K * 2u + (uint32_t)kc * 2u;
             ra[i] = load_chunk<VA>(rsrc_a, off, [&](int p) { return kc + p * VA < K; });
         }
-        const int valid_k = min(BK, K - k0);
-        const __amdgpu_buffer_rsrc_t rsrc_b =
-            make_rsrc(B + (size_t)k0 * (size_t)N, (uint32_t)valid_k * (uint32_t)N * 2u);
+        if constexpr (B_NK) {
 #pragma unroll
-        for (int r = 0; r < KB; ++r)
-            rb[r] = load_chunk<VB>(rsrc_b, b_off + (uint32_t)r * (uint32_t)N * 2u,
-                                   [&](int p) { return b_col + p * VB < N; });
+            for (int i = 0; i < BT_CHUNKS; ++i) {
+                const int q = tid + i * THREADS;
+                const int kc = k0 + (q % (BK / 8)) * 8;
+                const uint32_t off = (uint32_t)(q / (BK / 8)) * (uint32_t)K * 2u + (uint32_t)kc * 2u;
+                rb[i] = load_chunk<VB>(rsrc_bt, off, [&](int p) { return kc + p * VB < K; });
+            }
+        } else {
+            const int valid_k = min(BK, K - k0);
+            const __amdgpu_buffer_rsrc_t rsrc_b =
+                make_rsrc(B + (size_t)k0 * (size_t)N, (uint32_t)valid_k * (uint32_t)N * 2u);
+#pragma unroll
+            for (int r = 0; r < KB; ++r)
+                rb[r] = load_chunk<VB>(rsrc_b, b_off + (uint32_t)r * (uint32_t)N * 2u,
+                                       [&](int p) { return b_col + p * VB < N; });
+        }
     };
 
     auto lds_store = [&](int stage) {
@@ -341,24 +359,32 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 #pragma unroll
         for (int i = 0; i < Cfg::A_CHUNKS; ++i)
             *reinterpret_cast<u32x4*>(As + lds_off(a_row[i], a_chunk[i])) = ra[i];
-        // Transpose the KB x 8 piece of B (rows k, 8 columns n) into 8 rows of
-        // B^T with KB consecutive k each.  Halves n of row k sit in dword n / 2.
+        if constexpr (B_NK) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-            const int row = b_nb * 8 + n;
-            if constexpr (KB == 8) {
-                u32x4 v;
+            for (int i = 0; i < BT_CHUNKS; ++i) {
+                const int q = tid + i * THREADS;
+                *reinterpret_cast<u32x4*>(Bs + lds_off(q / (BK / 8), q % (BK / 8))) = rb[i];
+            }
+        } else {
+            // Transpose the KB x 8 piece of B (rows k, 8 columns n) into 8 rows of
+            // B^T with KB consecutive k each.  Halves n of row k sit in dword n / 2.
 #pragma unroll
-                for (int kp = 0; kp < 4; ++kp)
-                    v[kp] = __builtin_amdgcn_perm(rb[2 * kp + 1][n >> 1], rb[2 * kp][n >> 1], sel);
-                *reinterpret_cast<u32x4*>(Bs + lds_off(row, b_kb)) = v;
-            } else {
-                u32x2 v;
+            for (int n = 0; n < 8; ++n) {
+                const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+                const int row = b_nb * 8 + n;
+                if constexpr (KB == 8) {
+                    u32x4 v;
 #pragma unroll
-                for (int kp = 0; kp < 2; ++kp)
-                    v[kp] = __builtin_amdgcn_perm(rb[2 * kp + 1][n >> 1], rb[2 * kp][n >> 1], sel);
-                *reinterpret_cast<u32x2*>(Bs + lds_off(row, b_kb >> 1) + (b_kb & 1) * 8) = v;
+                    for (int kp = 0; kp < 4; ++kp)
+                        v[kp] = __builtin_amdgcn_perm(rb[2 * kp + 1][n >> 1], rb[2 * kp][n >> 1], sel);
+                    *reinterpret_cast<u32x4*>(Bs + lds_off(row, b_kb)) = v;
+                } else {
+                    u32x2 v;
+#pragma unroll
+                    for (int kp = 0; kp < 2; ++kp)
+                        v[kp] = __builtin_amdgcn_perm(rb[2 * kp + 1][n >> 1], rb[2 * kp][n >> 1], sel);
+                    *reinterpret_cast<u32x2*>(Bs + lds_off(row, b_kb >> 1) + (b_kb & 1) * 8) = v;
+                }
             }
         }
     };

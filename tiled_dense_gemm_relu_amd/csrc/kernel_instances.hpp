@@ -42,15 +42,15 @@ static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile1
                   dma_geom_matches<DmaTile128WT, kDma128W>,
               "host DMA tile geometry out of date");
 
-template <int DT, class Cfg>
+template <int DT, class Cfg, bool B_NK = false>
 void fill_row(const void** row)
 {
-    row[0] = (const void*)&gemm_relu_tiled<Cfg, DT, 8, 8>;
-    row[1] = (const void*)&gemm_relu_tiled<Cfg, DT, 4, 8>;
-    row[2] = (const void*)&gemm_relu_tiled<Cfg, DT, 8, 4>;
-    row[3] = (const void*)&gemm_relu_tiled<Cfg, DT, 4, 4>;
-    row[4] = (const void*)&gemm_relu_tiled<Cfg, DT, 2, 2>;
-    row[5] = (const void*)&gemm_relu_tiled<Cfg, DT, 1, 1>;
+    row[0] = (const void*)&gemm_relu_tiled<Cfg, DT, 8, 8, B_NK>;
+    row[1] = (const void*)&gemm_relu_tiled<Cfg, DT, 4, 8, B_NK>;
+    row[2] = (const void*)&gemm_relu_tiled<Cfg, DT, 8, 4, B_NK>;
+    row[3] = (const void*)&gemm_relu_tiled<Cfg, DT, 4, 4, B_NK>;
+    row[4] = (const void*)&gemm_relu_tiled<Cfg, DT, 2, 2, B_NK>;
+    row[5] = (const void*)&gemm_relu_tiled<Cfg, DT, 1, 1, B_NK>;
 }
 
 template <int DT, class KN, class NK>
@@ -68,6 +68,8 @@ DtypeKernels make_table()
     DtypeKernels t{};
     fill_row<DT, Tile256>(t.tiled[kTile256]);
     fill_row<DT, Tile128>(t.tiled[kTile128]);
+    fill_row<DT, Tile256, true>(t.tiled_nt[kTile256]);
+    fill_row<DT, Tile128, true>(t.tiled_nt[kTile128]);
     t.direct = (const void*)&gemm_relu_direct<DT>;
     t.dma[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256, DT, false>;
     t.dma[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256, DT, true>;

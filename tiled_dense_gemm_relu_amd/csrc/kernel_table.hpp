@@ -29,7 +29,10 @@ enum DmaId {
 };
 
 struct DtypeKernels {
+    // Register-staged kernels by TileId and load-width pair; tiled_nt reads B
+    // given as B^T, an (N, K) row-major array (its load width counts along K).
     const void* tiled[kNumTiles][kNumVecPairs];
+    const void* tiled_nt[kNumTiles][kNumVecPairs];
     const void* direct;
     const void* dma[kNumDma][2];   // LDS-DMA kernels by DmaId, [K % BK != 0]; need 8-element loads of A and B
     // The 256 LDS-DMA kernel with 4-byte DMA lanes for B (B rows of an even
