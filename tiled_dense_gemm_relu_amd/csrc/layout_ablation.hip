@@ -30,6 +30,7 @@
 #include <cstring>
 #include <random>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "gemm_relu_kernels.hpp"
@@ -37,9 +38,17 @@
 namespace {
 
 using namespace gemm_relu_hip;
-using Product = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true, true>;
-using Unswizzled = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, false, true>;
-using NoRemap = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true, false>;
+// The library's large tile with the swizzle or the remap switched off; every
+// other parameter (waves, MFMA shape, schedule) is the library's.
+template <bool SWIZZLE, bool REMAP>
+using Variant = DmaConfig<DmaTile256::BM, DmaTile256::BN, DmaTile256::BK, DmaTile256::STAGES, DmaTile256::WAVES_M,
+                          DmaTile256::WAVES_N, DmaTile256::GROUP_M, DmaTile256::A_LANE_BYTES,
+                          DmaTile256::B_LANE_BYTES, DmaTile256::B_KMAJOR, DmaTile256::PRODUCERS, SWIZZLE, REMAP,
+                          DmaTile256::MF, DmaTile256::EARLY_REFILL>;
+using Product = Variant<true, true>;
+using Unswizzled = Variant<false, true>;
+using NoRemap = Variant<true, false>;
+static_assert(std::is_same<Product, DmaTile256>::value, "the product variant is the library's kernel");
 
 #define CHECK(x)                                                                               \
     do {                                                                                       \
