@@ -1192,15 +1192,17 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // first), +3.3% at 2048^3 (128 tile), +1.3% at 1024^3 and +0.8% on the
     // 64 x 16384 x 8192 bf16 shape (64 tile).
     //  Early refill (ER) moves the DMAs into the last k-step, after the
-    //  barrier, where they follow the reads of the next stage: the barrier has
+    //  barrier, alternating with the reads of the next stage: the barrier has
     //  just freed the slot this step read (every wave's reads of it are done),
     //  so step g+S can go there a k-step sooner than in step g+1's first
     //  k-step.  With two 16x16 k-steps per stage (BK = 64) the DMAs of the
     //  first k-step land only a few MFMAs before the barrier that waits for
     //  them; early refill gives them a whole k-step more: 0.591 against
     //  0.665 ms at 8192^3 on zeros (full clock).  With four 32x32 k-steps per
-    //  stage it costs time (0.610 against 0.552 ms), so it is a per-tile choice.
-    constexpr bool ALTERNATE = !WS && !ER;
+    //  stage it costs time (0.610 against 0.552 ms), so it is a per-tile
+    //  choice.  After the barrier, alternating against all reads first: 1415
+    //  against 1396 TFLOP/s at the power cap (all DMAs first: 1367).
+    constexpr bool ALTERNATE = !WS;
     auto first_kstep_item = [](int u0) {
         constexpr int PAIRS = NQC < NF ? NQC : NF;
         if (!ALTERNATE) return u0;
@@ -1343,9 +1345,10 @@ using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny sh
 // few rows, many columns (with split-K): 4 waves of 64x64, 8 stages, 7 x 16 KiB of B in flight
 using DmaTile64x256 = DmaConfig<64, 256, 32, 8, 1, 4, 4>;
 // B given as B^T, (N, K) row-major.  The 256 tile on 16x16x32 with early
-// refill: 1451 TFLOP/s at 1747 MHz against 1327 at 1498 MHz on 32x32x16, in
-// the measurement above.
-using DmaTile256T = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, true, 0, true, true, 16, true>;
+// refill: 1451 TFLOP/s at 1747 MHz against 1327 at 1498 MHz on 32x32x16 (64x128
+// waves both, in the measurement above); 128x64 waves, as for B (K, N), gave
+// 1402 against 1388 for 64x128 on another box.
+using DmaTile256T = DmaConfig<256, 256, 64, 2, 2, 4, 4, 16, 16, true, 0, true, true, 16, true>;
 using DmaTile256K2T = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, true>;
 using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
 using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
