@@ -51,3 +51,16 @@ def test_write_table_round_trips(tmp_path):
     rows = [tuple(int(v) for v in m.group(1).split(","))
             for m in (re.match(r"\{(.*)\},\s*$", l.strip()) for l in path.read_text().splitlines()) if m]
     assert rows == [(8, 16, 24, 1, 1, 5, 6, 4)]
+
+
+def test_choose_plain_keeps_the_incumbent_within_the_margin():
+    final = {(9, 1): 0.0610, (5, 1): 0.0609, (5, 2): 0.0594}
+    # 5 is faster than the incumbent 9 by 0.2%: not enough to replace it
+    assert tune.choose_plain(final, incumbent=9) == (0.0610, (9, 1))
+    # a candidate more than 2% faster replaces it
+    final[(10, 1)] = 0.0590
+    assert tune.choose_plain(final, incumbent=9) == (0.0590, (10, 1))
+    # an incumbent that was not timed (or is not a plain candidate) does not count
+    assert tune.choose_plain({(9, 1): 0.05, (5, 1): 0.0499}, incumbent=3) == (0.0499, (5, 1))
+    # split candidates never become the plain choice
+    assert tune.choose_plain({(9, 1): 0.05, (5, 4): 0.01}, incumbent=9) == (0.05, (9, 1))

@@ -36,6 +36,10 @@ BEAM = 3
 # A split-K entry is kept only if it beats the plain choice by this factor
 # (it costs a workspace).
 SPLIT_MARGIN = 0.97
+# The plain configuration AUTO resolves to before the search (the table entry
+# or, for a new shape, the size rules) is kept unless another one beats it by
+# this factor, so that re-tuning does not flip choices on noise.
+PLAIN_MARGIN = 0.98
 MAX_WORKSPACE = 256 << 20          # split-K candidates needing more are not tried
 
 
@@ -109,6 +113,17 @@ def time_candidate(sets, M, N, K, dt, layout, config, splits, launches, ws):
     return times[len(times) // 2]          # median, ms
 
 
+def choose_plain(final, incumbent, margin=PLAIN_MARGIN):
+    """The plain (unsplit) configuration to record, from the final timings
+    {(config, parts): ms}: the fastest, unless the incumbent configuration was
+    timed and the fastest does not beat it by `margin`.  Returns (ms, (config, 1))."""
+    best = min((t, c) for c, t in final.items() if c[1] == 1)
+    inc = (incumbent, 1)
+    if inc in final and best[0] >= margin * final[inc]:
+        return final[inc], inc
+    return best
+
+
 def tune_shape(M, N, K, dtype, layout, log):
     import torch
     from . import binding, inputs
@@ -130,10 +145,15 @@ def tune_shape(M, N, K, dtype, layout, log):
         best = sorted((t, c) for c, t in pre.items() if kind(c))[:BEAM]
         for _, c in best:
             final[c] = time_candidate(sets, M, N, K, dt, layout, c[0], c[1], FINAL_LAUNCHES, ws)
-    plain = min((t, c) for c, t in final.items() if c[1] == 1)
+    # the current AUTO choice is always timed in the final round, so that it can be kept
+    incumbent = binding.selected_config(M, N, K, dt, binding.CONFIG_AUTO, b_layout=layout)["config_id"]
+    if (incumbent, 1) in pre and (incumbent, 1) not in final:
+        final[(incumbent, 1)] = time_candidate(sets, M, N, K, dt, layout, incumbent, 1, FINAL_LAUNCHES, ws)
+    plain = choose_plain(final, incumbent)
     split = min(((t, c) for c, t in final.items() if c[1] > 1), default=None)
     entry = {"M": M, "N": N, "K": K, "dtype": dtype, "b_layout": layout, "config": plain[1][0],
              "config_ms": plain[0], "splitk_config": plain[1][0], "splits": 1, "splitk_ms": plain[0],
+             "incumbent": incumbent,
              "prefilter_ms": {f"{c}x{s}": round(t, 5) for (c, s), t in pre.items()},
              "final_ms": {f"{c}x{s}": round(t, 5) for (c, s), t in final.items()}}
     if split is not None and split[0] < SPLIT_MARGIN * plain[0]:
