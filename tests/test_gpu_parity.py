@@ -473,3 +473,30 @@ def test_python_wrapper_rejects_bad_tensors():
         gr.gemm_relu(a.float(), a.t().contiguous().float())
     with pytest.raises(ValueError):
         gr.gemm_relu(a.cpu(), a.t().contiguous().cpu())
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("b_layout", [binding.B_KN, binding.B_NK])
+@pytest.mark.parametrize("c_off", [0, 4, 1])
+@pytest.mark.parametrize("shape", [(300, 264, 128), (300, 264, 136), (260, 260, 192)])
+def test_dma256_c_store_paths(shape, c_off, b_layout, dtype):
+    """The 256 tile's three ways of storing C: staged through LDS (N % 8 == 0, C 16-byte aligned),
+    8-byte pieces (N % 4 == 0, C 8-byte aligned) and single elements, with K % 64 == 0 and a K tail,
+    for both B layouts."""
+    M, N, K = shape
+    if b_layout == binding.B_KN and N % 8:
+        pytest.skip("B stored (K, N) with N % 8 != 0 takes the 4-byte-lane instance")
+    dt = gr.F16 if dtype == "fp16" else gr.BF16
+    a, b = inputs.integer_pair(M, N, K, DT[dtype], seed=7 + c_off)
+    want = oracle.gemm_relu(a, b, dtype)
+    cbuf = torch.full((M * N + c_off,), float("nan"), dtype=DT[dtype], device="cuda")
+    cv = cbuf[c_off:].view(M, N)
+    bdev = (b.t().contiguous() if b_layout == binding.B_NK else b).cuda()
+    cfg = gr.selected_config(M, N, K, dtype=dt, config=binding.CONFIG_DMA_256, c_ptr=cv.data_ptr(),
+                             b_layout=b_layout)
+    assert cfg["config_id"] == binding.CONFIG_DMA_256
+    say(f"[256 tile C stores] {shape} c_off={c_off} layout={b_layout} {dtype}")
+    gr.gemm_relu_ex(a.cuda(), bdev, out=cv, b_layout=b_layout, config=binding.CONFIG_DMA_256)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(cv), want)
+    assert torch.isnan(cbuf[:c_off]).all()          # nothing written before C
