@@ -334,8 +334,9 @@ __device__ __forceinline__ void store_block16(uint16_t* __restrict__ C, const fl
 // the 8 blocks of a 32-row x 64-column piece are written to the strip (lane l
 // of block (i, j): strip row 16(j % 2) + l % 16, columns 16(i % 4) + 4(l / 16)
 // .. +3), then stored as 16-byte pieces exactly as store_tile_staged does.
-// With the strip's chunk swizzle c ^ ((r >> 1) & 7), each 32-lane half of an
-// 8-byte write covers 16 rows x one 16-byte chunk: 64 distinct banks.
+// The strip keeps its chunk swizzle c ^ ((r >> 1) & 7); the 8-byte writes
+// show 4 bank-conflict cycles each in the SQ counters, as the 32x32 form's do
+// (1.0M cycles per 8192^3 launch against 103M LDS-active cycles).
 template <int DT, int FN, int FM>
 __device__ __forceinline__ void store_tile_staged16(uint16_t* __restrict__ C, const floatx4 (&acc)[FN][FM],
                                                     uint8_t* strip, int lane, int m_base, int n_base, int M, int N)
@@ -951,10 +952,11 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
 
     // KTAIL 2: thread t owns dwords 2(t & 1) and 2(t & 1) + 1 of the last
     // K-step's piece holding element K - 1 in row t / 2 of the tile's A rows
-    // (and of its B^T rows when B is stored (N, K)).  fix_issue loads them when
-    // that stage is filled (rows past M or N and dwords past K read as zero);
-    // fix_apply writes them over what the DMA put there, once the stage has
-    // landed for every wave.  A and B^T rows have the same length and swizzle.
+    // (and of its B^T rows when B is stored (N, K)).  fix_issue loads them, for
+    // the tile at (m0, n0), when that stage is filled (rows past M or N and
+    // dwords past K read as zero); fix_apply writes them over what the DMA put
+    // there, once the stage has landed for every wave.  A and B^T rows have the
+    // same length and swizzle.
     static_assert(KTAIL != 2 || (S == 2 && !WS && LA == 16 && Cfg::THREADS == 2 * BM &&
                                  (!Cfg::B_KMAJOR || (LB == 16 && Cfg::THREADS == 2 * BN && B_ROW == A_ROW))),
                   "KTAIL 2 layout");
@@ -971,9 +973,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         return u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs, fx_k < K ? off : kOobOffset, 0, 0),
                      __builtin_amdgcn_raw_buffer_load_b32(rs, fx_k + 2 < K ? off + 4u : kOobOffset, 0, 0)};
     };
-    auto fix_issue = [&]() {
-        fx_a = fix_load(A + (size_t)f_m0 * (size_t)K, min(BM, M - f_m0));
-        if constexpr (Cfg::B_KMAJOR) fx_b = fix_load(B + (size_t)f_n0 * (size_t)K, min(BN, N - f_n0));
+    auto fix_issue = [&](int m0, int n0) {
+        fx_a = fix_load(A + (size_t)m0 * (size_t)K, min(BM, M - m0));
+        if constexpr (Cfg::B_KMAJOR) fx_b = fix_load(B + (size_t)n0 * (size_t)K, min(BN, N - n0));
     };
     auto fix_apply = [&](int slot) {
         *reinterpret_cast<u32x2*>(smem + slot * Cfg::A_STAGE + fx_lds) = fx_a;
@@ -1133,15 +1135,27 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
 
     // Prologue: steps 0 .. S-2 (early refill: 0 .. S-1) in flight, step 0
     // landed, its first k-step read.
-    constexpr bool ER = Cfg::EARLY_REFILL && !WS && KTAIL != 2;
+    constexpr bool ER = Cfg::EARLY_REFILL && !WS;
     constexpr int PRO = ER ? S : S - 1;   // steps the prologue issues
-    bool fix_first = false;   // KTAIL 2 (S == 2): step 0 is a tile's last K-step
+    // KTAIL 2 (S == 2): fix_first: step 0 is a tile's last K-step.  fix_pending:
+    // a fix is loaded (or, in the prologue, due) and waits for the barrier
+    // before its stage is read.  With early refill the prologue fills step 1
+    // too; its fix, for the tile at (fx1_m0, fx1_n0), is loaded once step 0's
+    // has been applied, and applied at step 0's barrier.
+    bool fix_first = false, fix_pending = false;
+    int fx1_m0 = 0, fx1_n0 = 0;
     if (!WS || producer) {
 #pragma unroll
         for (int s = 0; s < PRO; ++s) {
             if constexpr (KFIX) {
-                fix_first = fill_is_last_kstep();
-                if (fix_first) fix_issue();
+                if (s == 0) {
+                    fix_first = fill_is_last_kstep();
+                    if (fix_first) fix_issue(f_m0, f_n0);
+                } else {
+                    fix_pending = fill_is_last_kstep();
+                    fx1_m0 = f_m0;
+                    fx1_n0 = f_n0;
+                }
             }
 #pragma unroll
             for (int q = 0; q < NQ; ++q) dma(s, q);
@@ -1152,6 +1166,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     lds_barrier();
     if constexpr (KFIX) {
         if (fix_first) fix_apply(0);
+        if (ER && fix_pending) fix_issue(fx1_m0, fx1_n0);
     }
     if constexpr (WS) {
         if (producer) {
@@ -1218,17 +1233,23 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         const int slot_fill = ER ? slot : (g + S - 1) & (S - 1);
         // KTAIL 2: the stage filled in this step (step g+1) is a tile's last
         // K-step; its straddling pieces are loaded now and rewritten at the
-        // step barrier.
-        bool fix_now = false;
-        if constexpr (KFIX) {
-            fix_now = fill_is_last_kstep();
-            if (fix_now) fix_issue();
+        // step barrier.  With early refill the stage filled after this step's
+        // barrier (step g+2) is the one; its pieces are loaded right after that
+        // barrier and rewritten at the next step's (the fix loads are vector
+        // loads, so the barrier's vmcnt wait covers them).
+        if constexpr (KFIX && !ER) {
+            fix_pending = fill_is_last_kstep();
+            if (fix_pending) fix_issue(f_m0, f_n0);
         }
         auto step_barrier = [&]() {
             if constexpr (!WS) wait_vmcnt<(S - 2) * NQ>();   // step g+1 landed (for this wave)
             lds_barrier();                                   // ... and for every wave
             if constexpr (KFIX) {
-                if (fix_now) fix_apply(slot_next);
+                if (fix_pending) fix_apply(slot_next);
+                if constexpr (ER) {
+                    fix_pending = fill_is_last_kstep();
+                    if (fix_pending) fix_issue(f_m0, f_n0);
+                }
             }
         };
 #pragma unroll
@@ -1332,10 +1353,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
 // (the ds_read_b64_tr_b16 side) for 64 columns instead of 128.
 using DmaTile256 = DmaConfig<256, 256, 64, 2, 2, 4, 4, 16, 16, false, 0, true, true, 16, true>;
 // K % 64 != 0 (KTAIL 1): 64x128 waves, whose K-tail masks fit in 254 VGPRs
-// (the 128x64 layout needs 256 and 12 bytes of scratch per lane).
+// (the 128x64 layout needs 256 and 12 bytes of scratch per lane).  KTAIL 2
+// (K % 8 != 0) fits in 254 with 128x64 waves and takes DmaTile256.
 using DmaTile256Tail = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, false, 0, true, true, 16, true>;
-// K % 8 != 0 (KTAIL 2, which has no early refill): 8 waves of 64x128 on 32x32x16.
-using DmaTile256K2 = DmaConfig<256, 256, 64, 2, 4, 2, 4>;
 // With 4-byte DMA lanes for B (K, N) rows of an even length but not a multiple
 // of 8, BK = 32 in 4 stages; A keeps 16-byte lanes where K % 8 == 0.
 using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;
@@ -1349,7 +1369,6 @@ using DmaTile64x256 = DmaConfig<64, 256, 32, 8, 1, 4, 4>;
 // waves both, in the measurement above); 128x64 waves, as for B (K, N), gave
 // 1402 against 1388 for 64x128 on another box.
 using DmaTile256T = DmaConfig<256, 256, 64, 2, 2, 4, 4, 16, 16, true, 0, true, true, 16, true>;
-using DmaTile256K2T = DmaConfig<256, 256, 64, 2, 4, 2, 4, 16, 16, true>;
 using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
 using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
 using DmaTile64x256T = DmaConfig<64, 256, 32, 8, 1, 4, 4, 16, 16, true>;

@@ -32,8 +32,7 @@ constexpr bool dw_geom_matches = Cfg::BM == kDma256DwGeom.bm && Cfg::BN == kDma2
 static_assert(dw_geom_matches<DmaTile256B4> && dw_geom_matches<DmaTile256AB4>,
               "host geometry of the 4-byte-lane 256 instances out of date");
 static_assert(dma_geom_matches<DmaTile256, kDma256> && dma_geom_matches<DmaTile256Tail, kDma256> &&
-                  dma_geom_matches<DmaTile256K2, kDma256> &&
-                  dma_geom_matches<DmaTile256K2T, kDma256> && dma_geom_matches<DmaTile128, kDma128> &&
+                  dma_geom_matches<DmaTile128, kDma128> &&
                   dma_geom_matches<DmaTile64, kDma64> && dma_geom_matches<DmaTile256T, kDma256> &&
                   dma_geom_matches<DmaTile128T, kDma128> &&
                   dma_geom_matches<DmaTile64T, kDma64> && dma_geom_matches<DmaTile64x256, kDma64x256> &&
@@ -83,7 +82,7 @@ DtypeKernels make_table()
     t.dma256_b4[0][1] = (const void*)&gemm_relu_dma<DmaTile256B4, DT, 1>;
     t.dma256_b4[1][0] = (const void*)&gemm_relu_dma<DmaTile256AB4, DT, 0>;
     t.dma256_b4[1][1] = (const void*)&gemm_relu_dma<DmaTile256AB4, DT, 1>;
-    t.dma256_kfix = (const void*)&gemm_relu_dma<DmaTile256K2, DT, 2>;
+    t.dma256_kfix = (const void*)&gemm_relu_dma<DmaTile256, DT, 2>;
     t.direct_nt = (const void*)&gemm_relu_direct<DT, true>;
     t.dma_nt[kDma256][0] = (const void*)&gemm_relu_dma<DmaTile256T, DT, false>;
     t.dma_nt[kDma256][1] = (const void*)&gemm_relu_dma<DmaTile256T, DT, true>;
@@ -91,7 +90,7 @@ DtypeKernels make_table()
     t.dma_nt[kDma128][1] = (const void*)&gemm_relu_dma<DmaTile128T, DT, true>;
     t.dma_nt[kDma64][0] = (const void*)&gemm_relu_dma<DmaTile64T, DT, false>;
     t.dma_nt[kDma64][1] = (const void*)&gemm_relu_dma<DmaTile64T, DT, true>;
-    t.dma_nt_kfix = (const void*)&gemm_relu_dma<DmaTile256K2T, DT, 2>;
+    t.dma_nt_kfix = (const void*)&gemm_relu_dma<DmaTile256T, DT, 2>;
     t.dma[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256, DT, false>;
     t.dma[kDma64x256][1] = (const void*)&gemm_relu_dma<DmaTile64x256, DT, true>;
     t.dma_nt[kDma64x256][0] = (const void*)&gemm_relu_dma<DmaTile64x256T, DT, false>;
