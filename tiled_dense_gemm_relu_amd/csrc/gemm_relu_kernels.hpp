@@ -9,28 +9,37 @@
 // software pipeline, a tile-level matrix-core product into an fp32 fragment,
 // an elementwise max(x, 0) on the fragment, a cast and a store.
 //
-// What changes for CDNA4:
-//  * The contraction runs on v_mfma_f32_32x32x16_{f16,bf16}: one wave64
-//    computes a 32x32 fp32 block per instruction from two 16-byte operand
-//    fragments per lane.  Both operands want 8 consecutive k values per lane.
-//    The large LDS-DMA tiles use v_mfma_f32_16x16x32 instead (16x16 blocks
-//    from 32 k), which does the same work for less energy: at the board's
-//    power cap that buys clock, and clock is what sets the large shapes'
-//    throughput (MfmaShape).  The notes below describe the 32x32 form.
-//  * B arrives N-contiguous, so it is transposed on its way into LDS (two
-//    v_perm_b32 per pair of halves), which leaves both LDS tiles K-contiguous:
-//    every operand fragment is then a single ds_read_b128.
+// Three kernels; the host picks one per call:
+//  * gemm_relu_dma, the LDS-DMA kernel (the default for every shape whose rows
+//    allow 16- or 4-byte loads): A and B tiles go from L2 into LDS through
+//    direct-to-LDS buffer loads in a ring of stages, B stays N-contiguous in
+//    LDS and is read K-packed with the gfx950 transpose read.  Its 256 x 256
+//    tiles run on 16x16x32 MFMAs, the smaller tiles on 32x32x16.
+//  * gemm_relu_tiled, the register-staged kernel, for rows of any length or
+//    alignment: loads go through VGPRs, and B is transposed on its way into
+//    LDS (two v_perm_b32 per pair of halves), which leaves both LDS tiles
+//    K-contiguous.
+//  * gemm_relu_direct: one wave per 32x32 block, operands straight from
+//    global memory; the fallback, and a structurally different second
+//    implementation for the tests.
+//
+// What changes for CDNA4, in all of them:
+//  * The contraction runs on MFMA: v_mfma_f32_32x32x16_{f16,bf16} computes a
+//    32x32 fp32 block per instruction, v_mfma_f32_16x16x32 a 16x16 one; both
+//    take two 16-byte operand fragments per lane, 8 consecutive k values each
+//    (MfmaShape).  At the board's power cap the 16x16x32 form does the same
+//    work for less energy, which buys clock.
 //  * The MFMA "A" operand is the B^T tile and the "B" operand is the A tile,
 //    so the MFMA output block is C^T: each lane then owns 4 consecutive
-//    columns of one row of C and stores them with one 8-byte store.
-//  * LDS rows are 128 bytes (BK = 64 halves = 8 chunks of 16 bytes).  The
-//    16-byte chunk c of row r sits at chunk position c ^ ((r ^ (r >> 3)) & 7).
-//    The XOR swizzle is the idea of "TileLang Guide: Composable Tiled AI Kernel
+//    columns of one row of C and stores them with one 8-byte store (or stages
+//    them through LDS into whole 128-byte row pieces).
+//  * LDS rows of K-contiguous tiles are 128 bytes (BK = 64 halves = 8 chunks
+//    of 16 bytes), and their 16-byte chunks are XOR-swizzled per row.  The
+//    XOR swizzle is the idea of "TileLang Guide: Composable Tiled AI Kernel
 //    Programming" (section "Automated Layout Inference and Bank Conflict
 //    Elimination") and of the zwxr.cn hands-on article, section 2.3 (shared
-//    memory and bank conflicts); this particular function is chosen for
-//    ds_read_b128 reading 16 consecutive rows at one logical chunk, which it
-//    spreads over 16 distinct 16-byte bank groups (a 256-byte bank window).
+//    memory and bank conflicts); the functions here are chosen for the
+//    gfx950 LDS reads each kernel issues (lds_off, a_swizzle, b_swizzle).
 //  * Global loads are buffer loads whose descriptor covers only the rows that
 //    exist: rows past M (for A) or past K (for B) read as zero in hardware;
 //    columns past K (A) or past N (B) are masked by sending the offset out of
@@ -208,7 +217,10 @@ __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rsrc, uint32_
 
 // ---------------------------------------------------------------- LDS layout
 
-// Byte offset of logical 16-byte chunk c (0..7) of row r in a 128-byte-row tile.
+// Byte offset of logical 16-byte chunk c (0..7) of row r in a 128-byte-row tile
+// of the register-staged kernel: chunk c of row r sits at chunk position
+// c ^ ((r ^ (r >> 3)) & 7).  A ds_read_b128 of 16 consecutive rows at one
+// logical chunk lands in 16 distinct 16-byte bank groups (a 256-byte window).
 __device__ __forceinline__ uint32_t lds_off(int r, int c)
 {
     return (uint32_t)(r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4));
@@ -582,9 +594,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 // MFMAs at no register cost.  This is the pages' multi-stage software
 // pipeline (T.Pipelined with several stages in flight), built from gfx950 LDS
 // DMA instead of cp.async/TMA.  The large instance (256x256x64, 2 stages)
-// runs 8 waves of 64x128, two per SIMD, so one wave's LDS and barrier waits
-// are covered by the other's MFMAs; the small instance (64x64x64, 8 stages)
-// keeps 7 stages of loads in flight for latency- and HBM-bound shapes.
+// runs 8 waves of 128x64 on 16x16x32 MFMAs, two per SIMD, so one wave's LDS
+// and barrier waits are covered by the other's MFMAs; the small instance
+// (64x64x64, 8 stages) keeps 7 stages of loads in flight for latency- and
+// HBM-bound shapes.
 //
 // LDS layout: all A stages first, then all B stages.
 //  * A stage: BM rows (m) x BK k, K-contiguous as in memory, rows of BK*2
@@ -592,18 +605,20 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_tiled(
 //    ds_read_b128 of 16 consecutive rows).
 //  * B stage: BK rows (k) x BN n, kept N-contiguous as it is in memory, rows
 //    of BN*2 bytes, chunks swizzled by b_swizzle.  MFMA operands need 8
-//    consecutive k per lane; ds_read_b64_tr_b16 gives them: within each group
-//    of 16 lanes, source lane s points at row s / 4, columns 4 (s % 4) .. +3 of
-//    a 4 x 16 block, and lane j receives the 4 k values of column j.
+//    consecutive k per lane; ds_read_b64_tr_b16 gives them 4 at a time:
+//    within each group of 16 lanes, source lane s points at row s / 4,
+//    columns 4 (s % 4) .. +3 of a 4 x 16 block, and lane j receives the 4 k
+//    values of column j.
 // A DMA instruction writes 1 KB of LDS at consecutive 16-byte slots (lane l at
 // base + 16 l); the swizzle is applied by choosing which global chunk lane l
 // fetches.
 //
-// One K-step is BK/16 MFMA k-steps; the work of each (the next k-step's
-// fragment reads and, in the first, the DMA of stage kt+STAGES-1) is spread
-// one group per MFMA.  Before the last k-step the wave waits for stage kt+1
-// and meets the other waves at the barrier, then reads stage kt+1's first
-// fragments while the last MFMAs of stage kt run.  The loop body has no
+// One K-step is BK/KSTEP MFMA k-steps (KSTEP = 16 or 32 k); the work of each
+// (the next k-step's fragment reads and, in the first, the DMA of stage
+// kt+STAGES-1; with early refill, in the last, that of stage kt+STAGES) is
+// spread one group per MFMA.  In the last k-step the wave waits for stage
+// kt+1 and meets the other waves at the barrier, then reads stage kt+1's
+// first fragments while the last MFMAs of stage kt run.  The loop body has no
 // branches: stages past the end are "loaded" through a zero-length buffer
 // descriptor (nothing is fetched).
 //
@@ -763,7 +778,7 @@ struct DmaConfig {
 };
 
 // The LDS-DMA kernel: block tile BM x BN x BK, a ring of STAGES LDS stages
-// filled by direct-to-LDS loads, WAVES_M x WAVES_N waves of 32x32 MFMA blocks.
+// filled by direct-to-LDS loads, WAVES_M x WAVES_N waves of MF x MF MFMA blocks.
 // KTAIL 0: K is a multiple of BK.  KTAIL 1: it is not, so the last stage is
 // partial and its A pieces past K are masked (K must still be a multiple of
 // the piece: 8 elements for 16-byte lanes, 2 for 4-byte lanes).  KTAIL 2: as
