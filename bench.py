@@ -41,9 +41,9 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "dma256_square_8192_fp16_traffi
 
 
 def measured_traffic(workload_name, kernel_name):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by the
-    copy-kernel calibration; None unless they were taken on this workload, this kernel and the
-    current kernel sources."""
+    """Bytes per launch beyond L2 (FETCH_SIZE: what the L2s fetch on misses, from the MALL or HBM,
+    plus WRITE_SIZE) from the committed rocprofv3 runs, scaled by the copy-kernel calibration;
+    None unless they were taken on this workload, this kernel and the current kernel sources."""
     try:
         with open(TRAFFIC_PROFILE) as f:
             prof = json.load(f)
