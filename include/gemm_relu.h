@@ -98,8 +98,9 @@ enum {
     GEMM_RELU_CONFIG_TILE_256 = 1,    /* 256x256x64 block tile, 4 waves, 2 LDS stages */
     GEMM_RELU_CONFIG_TILE_128 = 2,    /* 128x128x64 block tile, 4 waves, 2 LDS stages */
     GEMM_RELU_CONFIG_DMA_256 = 3,     /* 256x256x64 block tile, 8 waves, 2 LDS stages filled by
-                                         direct-to-LDS loads; 16x16x32 MFMAs (32x32x16 where
-                                         K % 8 != 0) */
+                                         direct-to-LDS loads, 16x16x32 MFMAs; with 4-byte DMA
+                                         lanes (rows that are not 16-byte multiples) 256x256x32 in
+                                         4 stages on 32x32x16 MFMAs */
     GEMM_RELU_CONFIG_DMA_128 = 4,     /* 128x128x64 block tile, 4 waves, 4 direct-to-LDS stages */
     GEMM_RELU_CONFIG_DMA_64 = 5,      /* 64x64x64 block tile, 4 waves, 8 direct-to-LDS stages
                                          (small, skinny and bandwidth-bound shapes) */
