@@ -19,6 +19,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libgemm_relu.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ABLATION_PATH = os.path.join(PKG, "layout_ablation")
+MFMA_FORM_PATH = os.path.join(PKG, "mfma_form")
 ARCH = "gfx950"
 
 SOURCES = ["gemm_relu_api.hip", "kernels_f16.hip", "kernels_bf16.hip"]
@@ -77,15 +78,17 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
-    # The layout-ablation measurement program (XOR swizzle on / off).
-    tmp = ABLATION_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, os.path.join(CSRC, "layout_ablation.hip"), "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for layout_ablation.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, ABLATION_PATH)
+    # The measurement programs: layout ablations (XOR swizzle, XCD remap on / off)
+    # and the power and clock of the two MFMA forms.
+    for src, path in (("layout_ablation.hip", ABLATION_PATH), ("mfma_form.hip", MFMA_FORM_PATH)):
+        tmp = path + f".tmp{os.getpid()}"
+        cmd = [hipcc(), *HIPCC_FLAGS, *extra, os.path.join(CSRC, src), "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        os.replace(tmp, path)
     if verbose:
-        print(f"built {LIB_PATH} and {ABLATION_PATH}")
+        print(f"built {LIB_PATH}, {ABLATION_PATH} and {MFMA_FORM_PATH}")
     return LIB_PATH
 
 
