@@ -10,19 +10,20 @@ import torch
 
 import oracle
 import tiled_dense_gemm_relu_amd as gr
-from tiled_dense_gemm_relu_amd import inputs
+from tiled_dense_gemm_relu_amd import binding, inputs
 
 from test_gpu_parity import bits
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kind", ["plain", "b_nk", "splitk", "splitk_noalloc"])
+@pytest.mark.parametrize("kind", ["plain", "b_nk", "dma256", "dma256_b_nk", "splitk", "splitk_noalloc"])
 def test_graph_replays_match_the_oracle(kind):
     M, N, K = 192, 320, 512
     dev = torch.device("cuda:0")
     a = torch.empty((M, K), dtype=torch.float16, device=dev)
-    b = torch.empty((N, K) if kind == "b_nk" else (K, N), dtype=torch.float16, device=dev)
+    nk = kind in ("b_nk", "dma256_b_nk")
+    b = torch.empty((N, K) if nk else (K, N), dtype=torch.float16, device=dev)
     c = torch.empty((M, N), dtype=torch.float16, device=dev)
     ws = torch.zeros(gr.selected_splitk_config(M, N, K, splits=4)["workspace_bytes"], dtype=torch.uint8,
                      device=dev)
@@ -32,6 +33,9 @@ def test_graph_replays_match_the_oracle(kind):
             gr.gemm_relu(a, b, out=c)
         elif kind == "b_nk":
             gr.gemm_relu_ex(a, b, out=c, b_layout=gr.B_NK)
+        elif kind.startswith("dma256"):
+            # the 256 tile (16x16x32 MFMAs, early refill), forced at this small shape
+            gr.gemm_relu_ex(a, b, out=c, b_layout=gr.B_NK if nk else gr.B_KN, config=binding.CONFIG_DMA_256)
         elif kind == "splitk":
             gr.gemm_relu_splitk(a, b, out=c, splits=4, workspace=ws)
         else:
@@ -50,7 +54,7 @@ def test_graph_replays_match_the_oracle(kind):
     for seed in (11, 12, 13):
         ah, bh = inputs.integer_pair(M, N, K, torch.float16, seed=seed)
         a.copy_(ah)
-        b.copy_(bh.t() if kind == "b_nk" else bh)
+        b.copy_(bh.t() if nk else bh)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
