@@ -77,17 +77,36 @@ def make_sets(w, n_sets, device, b_layout=binding.B_KN, data="normal"):
     return sets
 
 
-def _gpu_sysfs_dir():
-    """The sysfs device directory of the GPU (AMD vendor id with a shader-clock table), or None."""
+def _gpu_sysfs_dir(pci_addr=None, root="/sys/class/drm"):
+    """The sysfs device directory of the measured GPU: among the AMD cards with a shader-clock
+    table, the one whose PCI address ("dddd:bb:dd.f", the name of the device directory the card's
+    link points to) is `pci_addr`, else the first of them; None if there is none."""
     import glob
-    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+    cards = []
+    for d in sorted(glob.glob(os.path.join(root, "card*", "device"))):
         try:
             if open(os.path.join(d, "vendor")).read().strip() == "0x1002" and \
                     os.path.exists(os.path.join(d, "pp_dpm_sclk")):
-                return d
+                cards.append(d)
         except OSError:
             continue
-    return None
+    if pci_addr:
+        for d in cards:
+            if os.path.basename(os.path.realpath(d)).lower() == pci_addr.lower():
+                return d
+    return cards[0] if cards else None
+
+
+def _device_pci_addr():
+    """The PCI address of the current GPU as sysfs names it, from torch's device properties, or None
+    (no GPU, or a torch without those fields)."""
+    try:
+        if not torch.cuda.is_available():
+            return None
+        p = torch.cuda.get_device_properties(torch.cuda.current_device())
+        return f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    except (AttributeError, RuntimeError):
+        return None
 
 
 _SYSFS = None
@@ -100,7 +119,7 @@ def read_clocks():
     the board does not report is "unavailable"."""
     global _SYSFS
     if _SYSFS is None:
-        _SYSFS = _gpu_sysfs_dir() or ""
+        _SYSFS = _gpu_sysfs_dir(_device_pci_addr()) or ""
     out = {"sclk_mhz": "unavailable", "mclk_mhz": "unavailable", "power_w": "unavailable"}
     if not _SYSFS:
         return out
@@ -131,7 +150,7 @@ def read_power_cap():
     import glob
     global _SYSFS
     if _SYSFS is None:
-        _SYSFS = _gpu_sysfs_dir() or ""
+        _SYSFS = _gpu_sysfs_dir(_device_pci_addr()) or ""
     if not _SYSFS:
         return "unavailable"
     for f in sorted(glob.glob(os.path.join(_SYSFS, "hwmon", "hwmon*", "power1_cap"))):

@@ -92,3 +92,24 @@ def test_clock_readers_report_unavailable_without_a_gpu(monkeypatch):
     assert bench.read_clocks() == {"sclk_mhz": "unavailable", "mclk_mhz": "unavailable", "power_w": "unavailable"}
     assert bench.read_power_cap() == "unavailable"
     assert bench.power_clock_context(1.0, 2500.0, None)["sustained_sclk_mhz"] == "unavailable"
+
+
+def test_sysfs_card_is_chosen_by_pci_address(tmp_path):
+    # Two AMD cards whose device links point at their PCI directories: the one whose address is the
+    # measured GPU's is chosen; an unknown or missing address falls back to the first card.
+    import bench
+    drm, pci = tmp_path / "drm", tmp_path / "pci"
+    for card, addr in (("card0", "0000:03:00.0"), ("card1", "0000:83:00.0")):
+        dev = pci / addr
+        dev.mkdir(parents=True)
+        (dev / "vendor").write_text("0x1002\n")
+        (dev / "pp_dpm_sclk").write_text("0: 2400Mhz *\n")
+        (drm / card).mkdir(parents=True)
+        os.symlink(dev, drm / card / "device")
+    (drm / "card2").mkdir()                       # a card without a device link is skipped
+    chosen = bench._gpu_sysfs_dir("0000:83:00.0", root=str(drm))
+    assert os.path.realpath(chosen) == str(pci / "0000:83:00.0")
+    assert os.path.realpath(bench._gpu_sysfs_dir("0000:03:00.0", root=str(drm))) == str(pci / "0000:03:00.0")
+    assert os.path.realpath(bench._gpu_sysfs_dir("0000:99:00.0", root=str(drm))) == str(pci / "0000:03:00.0")
+    assert os.path.realpath(bench._gpu_sysfs_dir(None, root=str(drm))) == str(pci / "0000:03:00.0")
+    assert bench._gpu_sysfs_dir(None, root=str(tmp_path / "none")) is None

@@ -27,8 +27,11 @@
 // if the check fails.
 #include <hip/hip_runtime.h>
 
+#include <strings.h>
+
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
@@ -186,15 +189,25 @@ void fill_integer(std::vector<_Float16>& v, uint64_t seed)
     for (auto& x : v) x = (_Float16)(double)((int)(g.next() % 5) - 2);
 }
 
-std::string gpu_sysfs_dir()
+// The sysfs device directory of the measured GPU: among the AMD cards with a
+// shader-clock table, the one whose device link points at the PCI address
+// `pci_addr` ("dddd:bb:dd.f"), else the first of them; "" if there is none.
+std::string gpu_sysfs_dir(const std::string& pci_addr)
 {
+    std::string first;
     for (int c = 0; c < 64; ++c) {
         const std::string d = "/sys/class/drm/card" + std::to_string(c) + "/device";
         std::ifstream v(d + "/vendor");
         std::string s;
-        if (v >> s && s == "0x1002" && std::ifstream(d + "/pp_dpm_sclk").good()) return d;
+        if (!(v >> s && s == "0x1002" && std::ifstream(d + "/pp_dpm_sclk").good())) continue;
+        if (first.empty()) first = d;
+        char real[PATH_MAX];
+        if (!pci_addr.empty() && realpath(d.c_str(), real)) {
+            const char* base = std::strrchr(real, '/');
+            if (base && !strcasecmp(base + 1, pci_addr.c_str())) return d;
+        }
     }
-    return "";
+    return first;
 }
 
 int read_sclk_mhz(const std::string& dir)
@@ -411,7 +424,9 @@ int main(int argc, char** argv)
         std::fprintf(stderr, "needs a gfx950 GPU, found %s\n", prop.gcnArchName);
         return 2;
     }
-    const std::string dir = gpu_sysfs_dir();
+    char bus[32] = {0};
+    const std::string dir =
+        gpu_sysfs_dir(hipDeviceGetPCIBusId(bus, (int)sizeof bus, 0) == hipSuccess ? std::string(bus) : std::string());
     if (dir.empty()) std::fprintf(stderr, "no sysfs clock/power files: sclk and power are reported as -1\n");
     const int cus = prop.multiProcessorCount;
     int rc = 0;
