@@ -40,13 +40,39 @@ HIPCC_FLAGS = [
 KERNEL_SOURCES = ["gemm_relu_kernels.hpp", "kernel_instances.hpp", "kernels_f16.hip", "kernels_bf16.hip"]
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments and blank lines; string and character literals are kept
+    as they are (inline assembly strings hold sequences such as "\\n\\t")."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":                               # literal: copy through its closing quote
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):                 # line comment: drop to the end of the line
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):                 # block comment
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_digest() -> str:
-    """SHA-256 over the kernel sources: identifies the kernels a profile was taken on."""
+    """SHA-256 over the kernel sources with comments and blank lines removed: identifies the kernels
+    a profile was taken on, and stays the same when only comments change."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

@@ -96,11 +96,11 @@ __device__ __forceinline__ floatx16 mfma_32x32x16(u32x4 a, u32x4 b, floatx16 c)
 // Which 8 k a lane group takes only has to agree between the two operands;
 // the LDS-DMA kernel gives 16x16 lane group g = l / 16 the k-block
 // kgroup16(g) (see there).
-// At the board's power cap the 16x16x32 form sustains more flop per joule: an
-// MFMA-only loop on N(0, 0.12^2) fp16 register data ran 1934 TFLOP/s at
-// 1945 MHz against 1668 TFLOP/s at 1687 MHz for 32x32x16 (both 95% of the
-// peak at their clock, same board power); on zeros, at full clock, 742 W
-// against 889 W.
+// At the board's power cap the 16x16x32 form sustains more flop per joule: in
+// the mfma_form program's MFMA-only loop on N(0, 0.1^2) fp16 register data it
+// ran 1971 TFLOP/s at 2040 MHz and 1323 W against 1709 TFLOP/s at 1785 MHz and
+// 1300 W for 32x32x16 (0.67 against 0.76 pJ per flop); on zeros, at full
+// clock, 723 W against 866 W.
 template <int MF>
 struct MfmaShape;
 template <>
@@ -1361,9 +1361,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
 // whole 128-byte line (one L2 request instead of two): +2.7% at 8192^3,
 // measured in one process.  8 waves of 128x64 on 16x16x32 MFMAs with early
 // refill: on N(0, 0.1^2) fp16 8192^3, where the board's power cap sets the
-// clock, 1400 TFLOP/s at 1803 MHz against 1291 TFLOP/s at 1500 MHz for 8
-// waves of 64x128 on 32x32x16 MFMAs (the same box, alternating runs of 2.5 s
-// each); 64x128 waves on 16x16x32 gave 1384.  On zeros (full clock) the
+// clock, 1396 TFLOP/s at 1792 MHz against 1293 TFLOP/s at 1632 MHz for 8
+// waves of 64x128 on 32x32x16 MFMAs (the mfma_form program, alternating runs
+// of 2.5 s); on another box 1400 against 1291, where 64x128 waves on 16x16x32
+// gave 1384.  On zeros (full clock) the
 // 32x32 form is the faster one, 0.552 against 0.582 ms.  128x64 waves read B
 // (the ds_read_b64_tr_b16 side) for 64 columns instead of 128.
 using DmaTile256 = DmaConfig<256, 256, 64, 2, 2, 4, 4, 16, 16, false, 0, true, true, 16, true>;
