@@ -104,8 +104,9 @@ enum {
     GEMM_RELU_CONFIG_DMA_128 = 4,     /* 128x128x64 block tile, 4 waves, 4 direct-to-LDS stages */
     GEMM_RELU_CONFIG_DMA_64 = 5,      /* 64x64x64 block tile, 4 waves, 8 direct-to-LDS stages
                                          (small, skinny and bandwidth-bound shapes) */
-    GEMM_RELU_CONFIG_DMA_64x256 = 6,  /* 64x256x32 block tile, 4 waves, 8 direct-to-LDS stages
-                                         (few rows, many columns; meant for split-K) */
+    GEMM_RELU_CONFIG_DMA_64x256 = 6,  /* 64x256x32 block tile, 4 waves, 4 direct-to-LDS stages
+                                         (few rows, many columns: split-K, and M <= 64 with at
+                                         least 256 such tiles) */
     GEMM_RELU_CONFIG_DMA_256x128_WS = 7, /* 256x128x32 block tile, 4 direct-to-LDS stages, wave-
                                          specialised: 8 compute waves and 4 waves that only load */
     GEMM_RELU_CONFIG_DMA_32x32_WS = 8, /* 32x32x64 block tile, 4 direct-to-LDS stages, one compute

@@ -182,6 +182,24 @@ def test_few_tiles_deep_k_takes_32x32_producer_tiles():
     assert gr.selected_config(512, 512, 2052, config=8, b_layout=gr.B_NK)["config_id"] == 3
 
 
+def test_wide_decode_shapes_take_the_64x256_tile():
+    # at most 64 rows over 256 or more 64x256 tiles: the 64x256 tile, unsplit, 4 stages, staged C
+    cfg = gr.selected_config(64, 65536, 2048, dtype=gr.BF16)
+    assert (cfg["config_id"], cfg["block_m"], cfg["block_n"], cfg["block_k"], cfg["stages"], cfg["grid"],
+            cfg["splits"]) == (6, 64, 256, 32, 4, 256, 1)
+    assert cfg["lds_bytes"] == 4 * (64 + 256) * 32 * 2 + 4 * 4096
+    assert gr.selected_config(32, 65536, 4096, dtype=gr.BF16)["config_id"] == 6
+    assert gr.selected_config(1, 131072, 64)["config_id"] == 6
+    # 255 such tiles, more than 64 rows, or B stored (N, K): the other rules
+    assert gr.selected_config(64, 65280, 2048, dtype=gr.BF16)["config_id"] == 3
+    assert gr.selected_config(65, 65536, 2048, dtype=gr.BF16)["config_id"] == 3
+    assert gr.selected_config(64, 32768, 4096, dtype=gr.BF16)["config_id"] == 10
+    assert gr.selected_config(64, 65536, 2048, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] != 6
+    # without 16-byte loads of B: the 256 tile's 4-byte lanes (N even), else the register-staged tiles
+    assert gr.selected_config(64, 65538, 2048, dtype=gr.BF16)["config_id"] == 3
+    assert gr.selected_config(64, 65537, 2048, dtype=gr.BF16)["config_id"] in (1, 2)
+
+
 def test_b_nk_config_choice():
     big = nt_config(8192, 8192, 8192)
     assert (big["config_id"], big["vec_a"], big["vec_b"], big["b_layout"]) == (3, 8, 8, gr.B_NK)

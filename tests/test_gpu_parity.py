@@ -219,6 +219,35 @@ def test_skinny_64x16384x8192_bf16_full(integer):
         assert_within_tolerance(got, want, w.dtype)
 
 
+@pytest.mark.parametrize("integer", [False, True])
+@pytest.mark.parametrize("shape", [(64, 65536, 2048), (40, 65800, 1000)])
+def test_wide_decode_shapes(shape, integer):
+    # At most 64 rows over 256 or more 64x256 tiles: AUTO runs the 64x256 tile unsplit (4 stages,
+    # C staged through LDS).  The second shape has M, N and K tails (a partial last column tile and
+    # K % 32 != 0).  Sampled rows and entries against the oracle.
+    M, N, K = shape
+    assert gr.selected_config(M, N, K, dtype=gr.BF16)["config_id"] == binding.CONFIG_DMA_64x256
+    if integer:
+        a, b = inputs.integer_pair(M, N, K, torch.bfloat16, seed=M + N + K)
+    else:
+        a, b = inputs.normal_pair(M, N, K, torch.bfloat16, scale=0.05, seed=M + N + K)
+    say(f"[wide decode {shape} integer={integer}] GPU run")
+    got = run_gpu(a, b)
+    check_relu_invariants(got, "bf16")
+    rows = [0, 1, M // 2, M - 1]
+    want_rows = np.concatenate([oracle.gemm_relu_rows(a, b, "bf16", r, r + 1) for r in rows])
+    rng = np.random.default_rng(M + N + K)
+    ii = np.concatenate([rng.integers(0, M, 1024), np.full(64, M - 1)])
+    jj = np.concatenate([rng.integers(0, N, 1024), rng.integers(N - 256, N, 64)])
+    want_entries = oracle.gemm_relu_entries(a, b, "bf16", ii, jj)
+    if integer:
+        assert np.array_equal(got[rows], want_rows)
+        assert np.array_equal(got[ii, jj], want_entries)
+    else:
+        assert_within_tolerance(got[rows], want_rows, "bf16")
+        assert_within_tolerance(got[ii, jj], want_entries, "bf16")
+
+
 # ------------------------------------------------------------------ edge cases
 
 

@@ -47,3 +47,55 @@ def test_mfma_form_program():
     tiles = [l for l in lines if l["mode"] == "tile" and "form" in l]
     assert sorted(l["form"] for l in tiles) == ["16x16x32", "32x32x16"]
     assert all(l["tflops"] > 0 and l["launches"] > 0 for l in loops + tiles)
+
+
+STREAM_CEILING = os.path.join(os.path.dirname(PROGRAM), "stream_ceiling")
+
+
+def test_stream_ceiling_program():
+    """The skinny shape's streaming-ceiling program: three LDS-DMA read patterns and the library's
+    64x64 kernel (B stored (K, N) and (N, K)) each report a positive B rate, and each timed kernel's
+    C matches fp64 sums on sampled entries."""
+    if not os.path.exists(STREAM_CEILING):
+        pytest.fail(f"{STREAM_CEILING} is missing: build it with python -m tiled_dense_gemm_relu_amd.build")
+    res = subprocess.run([STREAM_CEILING, "--reps", "5"], capture_output=True, text=True, timeout=180)
+    assert res.returncode == 0, (res.stdout[-2000:], res.stderr[-2000:])
+    lines = [json.loads(l) for l in res.stdout.splitlines() if l.startswith("{")]
+    patterns = [l for l in lines if "pattern" in l]
+    assert [l["pattern"] for l in patterns] == ["contiguous", "strips", "strips_a"]
+    kernels = [l for l in lines if "kernel" in l]
+    assert [(l["b_layout"], l["workgroups"]) for l in kernels] == [("kn", 256), ("nk", 256)]
+    assert all(l["b_tbs"] > 0 for l in patterns + kernels)
+    assert [l["check"] for l in lines if "check" in l] == [{"b_layout": "kn", "sampled": 256, "mismatches": 0},
+                                                          {"b_layout": "nk", "sampled": 256, "mismatches": 0}]
+
+
+KERNEL_TIMELINE = os.path.join(os.path.dirname(PROGRAM), "kernel_timeline")
+
+
+def test_kernel_timeline_program():
+    """The kernel-timeline program times, per shape, the configuration AUTO picks for it; every
+    workgroup records every launch, the phases are non-negative and fit inside the launch span,
+    workgroup w runs on XCD w % 8 (the premise of the tile remap), and each shape's C matches
+    fp64 sums on sampled entries."""
+    from tiled_dense_gemm_relu_amd import binding as b
+    if not os.path.exists(KERNEL_TIMELINE):
+        pytest.fail(f"{KERNEL_TIMELINE} is missing: build it with python -m tiled_dense_gemm_relu_amd.build")
+    res = subprocess.run([KERNEL_TIMELINE, "--reps", "5"], capture_output=True, text=True, timeout=240)
+    assert res.returncode == 0, (res.stdout[-2000:], res.stderr[-2000:])
+    lines = [json.loads(l) for l in res.stdout.splitlines() if l.startswith("{")]
+    shapes = [l for l in lines if "shape" in l]
+    assert [l["shape"] for l in shapes] == ["square_256", "square_1024", "square_2048", "skinny_64x16384x8192",
+                                            "square_8192"]
+    for l in shapes:
+        dt = b.F16 if l["dtype"] == "fp16" else b.BF16
+        chosen = b.selected_config(l["M"], l["N"], l["K"], dt)["config_id"]
+        assert l["config"].startswith(f"{chosen}:"), (l["shape"], chosen, l["config"])
+        phases = [l[k] for k in ("ramp_us", "first_stage_us", "k_loop_us", "epilogue_us", "store_drain_us")]
+        assert all(p >= 0 for p in phases) and l["gap_us"] >= 0, l
+        assert l["first_stage_us"] + l["k_loop_us"] + l["epilogue_us"] + l["store_drain_us"] <= l["span_us"] * 1.05 + 0.05
+        assert 0 < l["span_us"] <= l["event_us"] * 1.5, l
+        # the tile remap's premise: the hardware dispatches workgroup w to XCD w % 8
+        assert l["xcd_is_wg_mod_8"] is True, l["shape"]
+        assert len(l["slowest_se_per_xcd"]) == 8
+    assert lines[-1]["checked"] is True

@@ -32,7 +32,7 @@ CONFIG_DMA_128x128_WS = 10
 CONFIG_NAMES = {CONFIG_DIRECT: "direct_32x32", CONFIG_TILE_256: "tile_256x256x64",
                 CONFIG_TILE_128: "tile_128x128x64", CONFIG_DMA_256: "dma_256x256x64_2stage",
                 CONFIG_DMA_128: "dma_128x128x64_4stage", CONFIG_DMA_64: "dma_64x64x64_8stage",
-                CONFIG_DMA_64x256: "dma_64x256x32_8stage", CONFIG_DMA_256x128_WS: "dma_256x128x32_4stage_ws",
+                CONFIG_DMA_64x256: "dma_64x256x32_4stage", CONFIG_DMA_256x128_WS: "dma_256x128x32_4stage_ws",
                 CONFIG_DMA_32x32_WS: "dma_32x32x64_4stage_ws", CONFIG_DMA_64x64_WS: "dma_64x64x64_4stage_ws",
                 CONFIG_DMA_128x128_WS: "dma_128x128x64_4stage_ws"}
 

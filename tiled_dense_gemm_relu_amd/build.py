@@ -20,6 +20,8 @@ LIB_NAME = "libgemm_relu.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ABLATION_PATH = os.path.join(PKG, "layout_ablation")
 MFMA_FORM_PATH = os.path.join(PKG, "mfma_form")
+STREAM_CEILING_PATH = os.path.join(PKG, "stream_ceiling")
+KERNEL_TIMELINE_PATH = os.path.join(PKG, "kernel_timeline")
 ARCH = "gfx950"
 
 SOURCES = ["gemm_relu_api.hip", "kernels_f16.hip", "kernels_bf16.hip"]
@@ -104,9 +106,12 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
-    # The measurement programs: layout ablations (XOR swizzle, XCD remap on / off)
-    # and the power and clock of the two MFMA forms.
-    for src, path in (("layout_ablation.hip", ABLATION_PATH), ("mfma_form.hip", MFMA_FORM_PATH)):
+    # The measurement programs: layout ablations (XOR swizzle, XCD remap on / off),
+    # the power and clock of the two MFMA forms, the skinny shape's streaming ceiling
+    # and the per-workgroup phase timeline of a launch.
+    programs = (("layout_ablation.hip", ABLATION_PATH), ("mfma_form.hip", MFMA_FORM_PATH),
+                ("stream_ceiling.hip", STREAM_CEILING_PATH), ("kernel_timeline.hip", KERNEL_TIMELINE_PATH))
+    for src, path in programs:
         tmp = path + f".tmp{os.getpid()}"
         cmd = [hipcc(), *HIPCC_FLAGS, *extra, os.path.join(CSRC, src), "-o", tmp]
         res = subprocess.run(cmd, capture_output=True, text=True)
@@ -114,7 +119,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
             raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
         os.replace(tmp, path)
     if verbose:
-        print(f"built {LIB_PATH}, {ABLATION_PATH} and {MFMA_FORM_PATH}")
+        print(f"built {LIB_PATH} and " + ", ".join(path for _, path in programs))
     return LIB_PATH
 
 

@@ -53,6 +53,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Timeline hooks of the LDS-DMA kernel.  They expand to nothing unless a
+// measurement program defines GEMM_RELU_TIMELINE before including this header
+// (the library never does): then GEMM_RELU_TIMELINE_BEGIN opens a record at
+// kernel entry, GEMM_RELU_MARK(p) stamps phase point p (1: the first stage is
+// in LDS for every wave; 2: the last unit's K loop is done; 3: its C stores
+// are issued) and GEMM_RELU_TIMELINE_END closes the record at exit.
+#ifndef GEMM_RELU_TIMELINE
+#define GEMM_RELU_TIMELINE_BEGIN
+#define GEMM_RELU_MARK(point)
+#define GEMM_RELU_TIMELINE_END
+#endif
+
 namespace gemm_relu_hip {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -809,6 +821,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN, NKS = Cfg::NKS;
     constexpr int A_ROW = Cfg::A_ROW, B_ROW = Cfg::B_ROW;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES + Cfg::C_STAGE_BYTES];
+    GEMM_RELU_TIMELINE_BEGIN
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1179,6 +1192,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         wait_vmcnt<(PRO - 1) * NQ>();
     }
     lds_barrier();
+    GEMM_RELU_MARK(1)
     if constexpr (KFIX) {
         if (fix_first) fix_apply(0);
         if (ER && fix_pending) fix_issue(fx1_m0, fx1_n0);
@@ -1313,6 +1327,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             // Fused epilogue of the finished unit: ReLU, round to the dtype,
             // masked store (with SPLITK, by the last part of the tile, after
             // the partial sums are combined); then start the next unit from zero.
+            GEMM_RELU_MARK(2)
             bool store = true;
             if constexpr (SPLITK) {
                 if (splits > 1) store = combine_parts(acc);
@@ -1342,6 +1357,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
                         }
                 }
             }
+            GEMM_RELU_MARK(3)
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -1353,6 +1369,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
         }
     }
     wait_vmcnt<0>();   // no LDS DMA may outlive the workgroup
+    GEMM_RELU_TIMELINE_END
 }
 
 // Instances.
@@ -1378,8 +1395,13 @@ using DmaTile256B4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 16, 4>;
 using DmaTile256AB4 = DmaConfig<256, 256, 32, 4, 4, 2, 4, 4, 4>;
 using DmaTile128 = DmaConfig<128, 128, 64, 4, 2, 2, 4>;   // mid shapes: 4 waves of 64x64
 using DmaTile64 = DmaConfig<64, 64, 64, 8, 2, 2, 4>;      // small and skinny shapes: 4 waves of 32x32, 8 stages
-// few rows, many columns (with split-K): 4 waves of 64x64, 8 stages, 7 x 16 KiB of B in flight
-using DmaTile64x256 = DmaConfig<64, 256, 32, 8, 1, 4, 4>;
+// At most 64 rows and many columns (split-K, and unsplit from 256 such tiles
+// on): 4 waves of 64x64, 4 stages.  Each tile reads 512 bytes of every B row.
+// This is HBM streaming, where less in flight per CU and no XCD remap measured
+// faster: on 64 x 65536 x 2048 bf16, 44.6 us against 48.7 for 8 stages with
+// the remap (5-9% on five such shapes); 64 x 16384 x 8192 in 4 parts, 54.6
+// against 55.1 us.
+using DmaTile64x256 = DmaConfig<64, 256, 32, 4, 1, 4, 4, 16, 16, false, 0, true, false>;
 // B given as B^T, (N, K) row-major.  The 256 tile on 16x16x32 with early
 // refill: 1451 TFLOP/s at 1747 MHz against 1327 at 1498 MHz on 32x32x16 (64x128
 // waves both, in the measurement above); 128x64 waves, as for B (K, N), gave
@@ -1387,7 +1409,11 @@ using DmaTile64x256 = DmaConfig<64, 256, 32, 8, 1, 4, 4>;
 using DmaTile256T = DmaConfig<256, 256, 64, 2, 2, 4, 4, 16, 16, true, 0, true, true, 16, true>;
 using DmaTile128T = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, true>;
 using DmaTile64T = DmaConfig<64, 64, 64, 8, 2, 2, 4, 16, 16, true>;
-using DmaTile64x256T = DmaConfig<64, 256, 32, 8, 1, 4, 4, 16, 16, true>;
+// B^T rows give a 64x256 tile only 64 bytes per row per K-step; 4 stages with
+// the remap measured best of 8 / 4 with / 4 without (64 x 65536 x 2048: 66.9
+// against 70.5 and 71.1 us; 64 x 16384 x 8192 in 2 parts: 76.6 against 81.1 and
+// 80.6).
+using DmaTile64x256T = DmaConfig<64, 256, 32, 4, 1, 4, 4, 16, 16, true>;
 // Wave-specialised: 8 compute waves of 64x64 and 4 DMA-only producer waves
 // (12 waves, 3 per SIMD: the 256x256 tile's accumulators leave no room for a
 // producer wave beside its compute waves).

@@ -60,7 +60,7 @@ constexpr TileGeom kDmaGeom[kNumDma] = {
     {256, 256, 64, 2, 512, 4, 32768},
     {128, 128, 64, 4, 256, 4, 16384},
     {64, 64, 64, 8, 256, 4, 0},
-    {64, 256, 32, 8, 256, 4, 0},
+    {64, 256, 32, 4, 256, 4, 16384},
     {256, 128, 32, 4, 768, 4, 32768},
     {32, 32, 64, 4, 320, 4, 0},
     {64, 64, 64, 4, 512, 4, 0},

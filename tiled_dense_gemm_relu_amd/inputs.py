@@ -53,7 +53,8 @@ class Workload:
 # The workload shapes: a small correctness case, the 1024^3 example shape with
 # 128x128x64 tiles, the 8192^3 compute-bound headline, a shape with ragged M, N
 # and K tails, a skinny decode-like bf16 shape that is HBM-bound, a deep-K
-# shape with few output tiles, the headline shape in bf16 and a mid-size square.
+# shape with few output tiles, the headline shape in bf16, a mid-size square
+# and a decode-like shape with many columns.
 WORKLOADS = {
     "small_256": Workload("small_256", 256, 256, 256, "fp16", 1.0, 1001, 1011),
     "square_1024": Workload("square_1024", 1024, 1024, 1024, "fp16", 1.0, 1002, 1012),
@@ -68,6 +69,9 @@ WORKLOADS = {
     "square_8192_bf16": Workload("square_8192_bf16", 8192, 8192, 8192, "bf16", 0.1, 1007, 1017),
     # a mid-size square: 128x128 tiles fill the CUs, 256x256 ones do not
     "square_2048": Workload("square_2048", 2048, 2048, 2048, "fp16", 0.1, 1008, 1018),
+    # decode-like with many columns (256 tiles of 64x256): HBM-bound on B, like the skinny shape
+    "wide_decode_64x65536x2048": Workload("wide_decode_64x65536x2048", 64, 65536, 2048, "bf16", 0.05,
+                                          1009, 1019),
 }
 
 
