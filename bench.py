@@ -455,6 +455,7 @@ def main():
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_DMA_64x256, 4),
                 ("wide_decode_64x65536x2048", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("wide_decode_64x65536x2048", binding.B_NK, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("deep_512x512x16384", binding.B_KN, binding.CONFIG_AUTO, 0),
                 ("square_2048", binding.B_KN, binding.CONFIG_AUTO, None),

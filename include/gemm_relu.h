@@ -226,7 +226,8 @@ int gemm_relu_query_config_ex(const void* A, const void* B, const void* C, int64
  * configurations, or when the count resolves to 1, the call is gemm_relu_ex
  * (workspace unused, may be NULL).  With GEMM_RELU_CONFIG_AUTO and n >= 1 the
  * tile is always one that splits: the tuned table's, if it splits, else by the
- * size rules, which take DMA_64x256 for M <= 64 when its loads are possible.
+ * size rules, which take DMA_64x256 for M <= 64 when its loads are possible
+ * and B is stored (K, N).
  *
  * workspace: device memory of at least gemm_relu_config_t.workspace_bytes
  * (from gemm_relu_query_splitk with the same arguments), 256-byte aligned,

@@ -190,11 +190,15 @@ def test_wide_decode_shapes_take_the_64x256_tile():
     assert cfg["lds_bytes"] == 4 * (64 + 256) * 32 * 2 + 4 * 4096
     assert gr.selected_config(32, 65536, 4096, dtype=gr.BF16)["config_id"] == 6
     assert gr.selected_config(1, 131072, 64)["config_id"] == 6
-    # 255 such tiles, more than 64 rows, or B stored (N, K): the other rules
+    # 255 such tiles or more than 64 rows: the other rules
     assert gr.selected_config(64, 65280, 2048, dtype=gr.BF16)["config_id"] == 3
     assert gr.selected_config(65, 65536, 2048, dtype=gr.BF16)["config_id"] == 3
     assert gr.selected_config(64, 32768, 4096, dtype=gr.BF16)["config_id"] == 10
-    assert gr.selected_config(64, 65536, 2048, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] != 6
+    # B stored (N, K), at most 64 rows: the 64x64 producer tile (32x32 when 64x64 tiles are few)
+    assert gr.selected_config(64, 65536, 2048, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] == 9
+    assert gr.selected_config(16, 32768, 8192, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] == 9
+    assert gr.selected_config(64, 4096, 8192, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] == 8
+    assert gr.selected_config(65, 65536, 2048, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] == 3
     # without 16-byte loads of B: the 256 tile's 4-byte lanes (N even), else the register-staged tiles
     assert gr.selected_config(64, 65538, 2048, dtype=gr.BF16)["config_id"] == 3
     assert gr.selected_config(64, 65537, 2048, dtype=gr.BF16)["config_id"] in (1, 2)
@@ -357,9 +361,11 @@ def test_explicit_parts_are_never_dropped_by_the_tuned_table():
     untuned = gr.selected_splitk_config(2048, 2048, 2048 + 8, splits=4)
     assert (untuned["config_id"], untuned["splits"]) == (4, 4)
     # the skinny shape with B stored (N, K) is tuned unsplit on the 64x64 producer tile; asked for
-    # 2 parts it takes the 64x256 tile of the size rules for M <= 64
+    # 2 parts it takes the 64x64 tile that splits (the 64x256 rule for M <= 64 is for B (K, N))
     sk = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16, splits=2, b_layout=gr.B_NK)
-    assert (sk["config_id"], sk["splits"]) == (6, 2)
+    assert (sk["config_id"], sk["splits"]) == (5, 2)
+    sk = gr.selected_splitk_config(64, 16384, 8192 + 64, dtype=gr.BF16, b_layout=gr.B_NK)
+    assert (sk["config_id"], sk["splits"]) == (9, 1)   # untuned: 256 tiles of 64x64 need no parts
     # with the parts left to the library, the table still decides
     sk = gr.selected_splitk_config(64, 16384, 8192, dtype=gr.BF16, b_layout=gr.B_NK)
     assert (sk["config_id"], sk["splits"]) == (9, 1)

@@ -156,6 +156,34 @@ def test_b_nk_nothing_written_outside_c(config):
     assert_within_tolerance(raw[guard:guard + M * N].reshape(M, N), oracle.gemm_relu(a, b, "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("integer", [False, True])
+@pytest.mark.parametrize("shape", [(64, 65536, 2048), (40, 65800, 1000)])
+def test_b_nk_wide_decode_shapes(shape, integer):
+    # At most 64 rows with B^T: AUTO takes the 64x64 producer tile whatever the tile count (the
+    # second shape has M, N and K tails).  Sampled rows and entries against the oracle.
+    M, N, K = shape
+    assert gr.selected_config(M, N, K, dtype=gr.BF16, b_layout=gr.B_NK)["config_id"] == binding.CONFIG_DMA_64x64_WS
+    if integer:
+        a, b = inputs.integer_pair(M, N, K, torch.bfloat16, seed=M + N + K + 1)
+    else:
+        a, b = inputs.normal_pair(M, N, K, torch.bfloat16, scale=0.05, seed=M + N + K + 1)
+    say(f"[B^T wide decode {shape} integer={integer}] GPU run")
+    got = run_nk(a, b)
+    check_relu_invariants(got, "bf16")
+    rows = [0, 1, M // 2, M - 1]
+    want_rows = np.concatenate([oracle.gemm_relu_rows(a, b, "bf16", r, r + 1) for r in rows])
+    rng = np.random.default_rng(M + N + K + 1)
+    ii = np.concatenate([rng.integers(0, M, 1024), np.full(64, M - 1)])
+    jj = np.concatenate([rng.integers(0, N, 1024), rng.integers(N - 64, N, 64)])
+    want_entries = oracle.gemm_relu_entries(a, b, "bf16", ii, jj)
+    if integer:
+        assert np.array_equal(got[rows], want_rows)
+        assert np.array_equal(got[ii, jj], want_entries)
+    else:
+        assert_within_tolerance(got[rows], want_rows, "bf16")
+        assert_within_tolerance(got[ii, jj], want_entries, "bf16")
+
+
 def test_b_nk_k_zero_and_empty():
     a = torch.empty((37, 0), dtype=torch.float16, device="cuda")
     bt = torch.empty((53, 0), dtype=torch.float16, device="cuda")

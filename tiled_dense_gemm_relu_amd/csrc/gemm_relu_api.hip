@@ -160,8 +160,10 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         }
     }
     // With split-K on offer, a block of at most 64 rows takes the 64x256 tile:
-    // its K parts restore the parallelism the few tiles lack.
-    if (chosen == GEMM_RELU_CONFIG_AUTO && splits_req >= 0 && full_vectors && M <= 64)
+    // its K parts restore the parallelism the few tiles lack.  Not for B stored
+    // (N, K), where a 64x256 tile reads only 64 bytes of each B^T row per K-step
+    // (the skinny shape in 2 parts: 76.6 us); the 64x64 tile takes it below.
+    if (chosen == GEMM_RELU_CONFIG_AUTO && splits_req >= 0 && full_vectors && M <= 64 && !plan->b_nk)
         chosen = GEMM_RELU_CONFIG_DMA_64x256;
     // The plain entry point's small tiles take producer waves: 64x64 tiles
     // (measured faster at 1024^3), or, where 64x64 tiles would leave at least
@@ -187,8 +189,15 @@ int make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
         if (chosen == GEMM_RELU_CONFIG_AUTO) {
             const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
             const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
+            // At most 64 rows: the small tiles whatever the tile count.  Their B^T
+            // row pieces are as long as the larger tiles' and no tile rows are
+            // wasted: 64 x 65536 x 2048 bf16 took 63.3 us against 78.7 on the 256
+            // tile, 32 x 65536 x 4096 109 against 141, 16 x 32768 x 8192 111
+            // against 127 on the 128x128 tile.
             if (!dword_vectors)
                 chosen = t256 >= 192 ? GEMM_RELU_CONFIG_TILE_256 : GEMM_RELU_CONFIG_TILE_128;
+            else if (M <= 64 && full_vectors)
+                chosen = small_dma;
             else if (t256 >= 192 || !full_vectors)
                 chosen = GEMM_RELU_CONFIG_DMA_256;
             else
