@@ -62,7 +62,7 @@ def test_stream_ceiling_program():
     assert res.returncode == 0, (res.stdout[-2000:], res.stderr[-2000:])
     lines = [json.loads(l) for l in res.stdout.splitlines() if l.startswith("{")]
     patterns = [l for l in lines if "pattern" in l]
-    assert [l["pattern"] for l in patterns] == ["contiguous", "strips", "strips_a"]
+    assert [l["pattern"] for l in patterns] == ["contiguous", "strips", "strips_a", "strips_pitch_plus_128"]
     kernels = [l for l in lines if "kernel" in l]
     assert [(l["b_layout"], l["workgroups"]) for l in kernels] == [("kn", 256), ("nk", 256)]
     assert all(l["b_tbs"] > 0 for l in patterns + kernels)

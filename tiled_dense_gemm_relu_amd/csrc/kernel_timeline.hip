@@ -24,9 +24,10 @@
 // and the distribution of workgroup exit times after the launch's first entry
 // (over all workgroups and launches, and its median per XCD), with where the
 // late workgroups ran: each workgroup also records its XCD, shader engine and
-// CU (the XCC_ID and HW_ID hardware registers), and the program lists, per XCD,
-// the shader engine whose workgroups exit last, and every workgroup whose
-// median exit is more than 15% after the median workgroup's.
+// CU (the XCC_ID and HW_ID hardware registers) and its last tile, and the
+// program lists, per XCD, the shader engine whose workgroups exit last, and
+// every workgroup whose median exit is more than 15% after the median
+// workgroup's, with its tile origin and where its columns start in a B row.
 // A sampled check of C against fp64 sums follows each shape.
 //
 // Usage: kernel_timeline [--reps N] [--shape NAME]
@@ -46,7 +47,7 @@
 
 namespace timeline {
 __device__ unsigned* g_count;             // per workgroup: launches recorded so far
-__device__ unsigned long long* g_rec;     // [launch][workgroup][6]: real-time stamps, placement
+__device__ unsigned long long* g_rec;     // [launch][workgroup][7]: real-time stamps, placement, tile
 __device__ unsigned g_max_launches;
 }  // namespace timeline
 
@@ -54,12 +55,14 @@ __device__ unsigned g_max_launches;
     unsigned long long gr_tl[4] = {__builtin_amdgcn_s_memrealtime(), 0ull, 0ull, 0ull};            \
     const unsigned gr_launch = timeline::g_count[blockIdx.x];
 #define GEMM_RELU_MARK(point) gr_tl[point] = __builtin_amdgcn_s_memrealtime();
-// Record: 5 stamps, then where the workgroup ran: XCC_ID (hardware register
-// 20) in bits 16 and up, and the low half of HW_ID (hardware register 4: CU in
-// bits 8-11, shader array in bit 12, shader engine in bits 13-15).
+// Record: 5 stamps; where the workgroup ran: XCC_ID (hardware register 20) in
+// bits 16 and up, and the low half of HW_ID (hardware register 4: CU in bits
+// 8-11, shader array in bit 12, shader engine in bits 13-15); and the origin of
+// the tile it computed last (the hooks expand inside gemm_relu_dma, whose
+// c_m0 / c_n0 hold it), m0 in the high 32 bits.
 #define GEMM_RELU_TIMELINE_END                                                                      \
     if (threadIdx.x == 0 && gr_launch < timeline::g_max_launches) {                                 \
-        unsigned long long* gr_r = timeline::g_rec + ((size_t)gr_launch * gridDim.x + blockIdx.x) * 6; \
+        unsigned long long* gr_r = timeline::g_rec + ((size_t)gr_launch * gridDim.x + blockIdx.x) * 7; \
         gr_r[0] = gr_tl[0];                                                                         \
         gr_r[1] = gr_tl[1];                                                                         \
         gr_r[2] = gr_tl[2];                                                                         \
@@ -67,6 +70,7 @@ __device__ unsigned g_max_launches;
         gr_r[4] = __builtin_amdgcn_s_memrealtime();                                                 \
         gr_r[5] = ((unsigned long long)(__builtin_amdgcn_s_getreg(20 | (31 << 11)) & 0xffffu) << 16) |  \
                   (__builtin_amdgcn_s_getreg(4 | (31 << 11)) & 0xffffu);                            \
+        gr_r[6] = ((unsigned long long)(unsigned)c_m0 << 32) | (unsigned)c_n0;                      \
         timeline::g_count[blockIdx.x] = gr_launch + 1;                                              \
     }
 
@@ -85,7 +89,7 @@ using namespace gemm_relu_hip;
         }                                                                                           \
     } while (0)
 
-constexpr int kMaxLaunches = 256, kMaxGrid = 1024, kSets = 3, kWarm = 3, kRec = 6;
+constexpr int kMaxLaunches = 256, kMaxGrid = 1024, kSets = 3, kWarm = 3, kRec = 7;
 
 // splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
 // generators", 2014) and the Box-Muller transform.
@@ -237,6 +241,7 @@ int run(const Shape& sh, int reps, int cus, double ticks_per_us)
     std::vector<double> exits, xcd_exits[8];
     std::vector<std::vector<double>> wg_exits(grid);
     std::vector<unsigned> place(grid);   // placement of each workgroup in the last launch
+    std::vector<unsigned long long> tile(grid);   // and its last tile's origin (m0 << 32 | n0)
     for (int l = kWarm; l < kWarm + reps; ++l) {
         const unsigned long long* r = &hrec[(size_t)l * grid * kRec];
         unsigned long long t0 = ~0ull, t0_max = 0, t4 = 0;
@@ -254,6 +259,7 @@ int run(const Shape& sh, int reps, int cus, double ticks_per_us)
         for (int w = 0; w < grid; ++w) {
             exits.push_back(us(t0, r[(size_t)w * kRec + 4]));
             place[w] = (unsigned)r[(size_t)w * kRec + 5];
+            tile[w] = r[(size_t)w * kRec + 6];
             xcd_exits[(place[w] >> 16) & 7].push_back(exits.back());
             wg_exits[w].push_back(exits.back());
         }
@@ -306,9 +312,11 @@ int run(const Shape& sh, int reps, int cus, double ticks_per_us)
     bool first_slow = true;
     for (int w = 0; w < grid; ++w)
         if (wg_p50[w] > 1.15 * typical) {
-            std::printf("%s{\"wg\": %d, \"xcd\": %u, \"se\": %u, \"cu\": %u, \"exit_p50_us\": %.2f}",
+            // B stored (K, N): the tile's columns start at byte 2 n0 of every B row
+            std::printf("%s{\"wg\": %d, \"xcd\": %u, \"se\": %u, \"cu\": %u, \"m0\": %u, \"n0\": %u, "
+                        "\"b_row_byte\": %u, \"exit_p50_us\": %.2f}",
                         first_slow ? "" : ", ", w, (place[w] >> 16) & 7, (place[w] >> 13) & 7, (place[w] >> 8) & 15,
-                        wg_p50[w]);
+                        (unsigned)(tile[w] >> 32), (unsigned)tile[w], 2u * (unsigned)tile[w], wg_p50[w]);
             first_slow = false;
         }
     std::printf("]}\n");

@@ -13,6 +13,12 @@
 //               pattern);
 //   strips_a    the same, with an 8 KiB step of a 1 MiB L2-resident buffer read
 //               beside each B step (the kernel's A tiles);
+//   strips_pitch_plus_128
+//               the strips pattern over the same bytes laid out with a row
+//               pitch of 32 KiB + 128 B: with the 32 KiB (power-of-two) pitch,
+//               the 128-byte slot at byte 384 of every KiB of every row sits on
+//               a narrower part of the memory system, and the workgroups that
+//               read it set the pace;
 // and then the library's kernels for the shape (the 64 x 64 tile with producer
 // waves that its tuned table picks) on the same buffers, which hold N(0, 0.05^2)
 // bf16 values as the workload's inputs do: with B stored (K, N), its 128-byte
@@ -51,6 +57,8 @@ using namespace gemm_relu_hip;
 
 constexpr int kRowBytes = 32768, kRows = 8192;           // B: 8192 rows of 16384 bf16
 constexpr size_t kBBytes = (size_t)kRowBytes * kRows;    // 256 MiB
+constexpr int kPaddedPitch = kRowBytes + 128;            // the padded layout's row pitch
+constexpr size_t kBufBytes = (size_t)kPaddedPitch * kRows;   // room for either layout
 constexpr int kARowBytes = 16384, kARows = 64;           // A: 64 rows of 8192 bf16 (1 MiB)
 constexpr int kWaves = 4, kInFlight = 16;                // DMA instructions (1 KiB each) per wave in flight
 constexpr int kGroups = 256;
@@ -70,13 +78,14 @@ struct DmaRing {
     }
 };
 
-template <int MODE>   // 0 contiguous, 1 strips, 2 strips with the A stream
+template <int MODE>   // 0 contiguous, 1 strips, 2 strips with the A stream, 3 strips at the padded pitch
 __global__ __launch_bounds__(64 * kWaves) void stream_b(const uint8_t* __restrict__ b, const uint8_t* __restrict__ a,
                                                         unsigned* __restrict__ out)
 {
+    constexpr uint32_t pitch = MODE == 3 ? kPaddedPitch : kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * kInFlight * 1024];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int32x4_t rb = rsrc_words(b, (uint32_t)kBBytes), ra = rsrc_words(a, kARowBytes * kARows);
+    const int32x4_t rb = rsrc_words(b, (uint32_t)kBufBytes), ra = rsrc_words(a, kARowBytes * kARows);
     DmaRing ring{(uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + wave * kInFlight * 1024};
     if constexpr (MODE == 0) {
         // 1 KiB pieces: workgroup g, wave w takes pieces g*kWaves + w, + kGroups*kWaves, ...
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(64 * kWaves) void stream_b(const uint8_t* __restric
         // 8 rows x 128 bytes per instruction: lane l reads row 8 g + l / 8, bytes 16 (l % 8) of the strip
         const uint32_t col = blockIdx.x * 128u + (lane & 7) * 16u;
         for (int g = wave; g < kRows / 8; g += kWaves) {
-            ring.issue(rb, (uint32_t)(g * 8 + (lane >> 3)) * kRowBytes + col);
+            ring.issue(rb, (uint32_t)(g * 8 + (lane >> 3)) * pitch + col);
             if constexpr (MODE == 2) {
                 // A: rows (g % 8) * 8 + l / 8 of 64, the 128-byte piece (g / 8) % 128 of each
                 const uint32_t off = (uint32_t)((g & 7) * 8 + (lane >> 3)) * kARowBytes + ((g >> 3) & 127) * 128u +
@@ -241,7 +250,7 @@ int main(int argc, char** argv)
     uint8_t *b[3], *a;
     uint16_t* c;
     unsigned* flag;
-    for (auto& p : b) CHECK(hipMalloc(&p, kBBytes));
+    for (auto& p : b) CHECK(hipMalloc(&p, kBufBytes));
     CHECK(hipMalloc(&a, kARowBytes * kARows));
     CHECK(hipMalloc(&c, (size_t)64 * 16384 * 2));
     CHECK(hipMalloc(&flag, sizeof(unsigned)));
@@ -252,12 +261,13 @@ int main(int argc, char** argv)
     fill_normal_bf16(host_a, 0.05, 1);
     for (auto& p : b) CHECK(hipMemcpy(p, host.data(), kBBytes, hipMemcpyHostToDevice));
     CHECK(hipMemcpy(a, host_a.data(), kARowBytes * kARows, hipMemcpyHostToDevice));
-    const char* names[] = {"contiguous", "strips", "strips_a"};
-    for (int mode = 0; mode < 3; ++mode) {
+    const char* names[] = {"contiguous", "strips", "strips_a", "strips_pitch_plus_128"};
+    for (int mode = 0; mode < 4; ++mode) {
         auto launch = [&](int i) {
             if (mode == 0) stream_b<0><<<kGroups, 64 * kWaves>>>(b[i % 3], a, flag);
             else if (mode == 1) stream_b<1><<<kGroups, 64 * kWaves>>>(b[i % 3], a, flag);
-            else stream_b<2><<<kGroups, 64 * kWaves>>>(b[i % 3], a, flag);
+            else if (mode == 2) stream_b<2><<<kGroups, 64 * kWaves>>>(b[i % 3], a, flag);
+            else stream_b<3><<<kGroups, 64 * kWaves>>>(b[i % 3], a, flag);
         };
         std::printf("{\"pattern\": \"%s\", \"workgroups\": %d, \"b_tbs\": %.3f}\n", names[mode], kGroups,
                     rate(launch, reps) / 1e12);
