@@ -453,6 +453,7 @@ def main():
                 ("square_1024", binding.B_KN, binding.CONFIG_DMA_128, None),     # the pages' 128x128x64 tile
                 ("ragged_4000x11000x4100", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_AUTO, None),
+                ("skinny_64x16384x8192", binding.B_NK, binding.CONFIG_AUTO, None),
                 ("skinny_64x16384x8192", binding.B_KN, binding.CONFIG_DMA_64x256, 4),
                 ("wide_decode_64x65536x2048", binding.B_KN, binding.CONFIG_AUTO, None),
                 ("wide_decode_64x65536x2048", binding.B_NK, binding.CONFIG_AUTO, None),

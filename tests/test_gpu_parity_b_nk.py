@@ -184,6 +184,28 @@ def test_b_nk_wide_decode_shapes(shape, integer):
         assert_within_tolerance(got[ii, jj], want_entries, "bf16")
 
 
+@pytest.mark.parametrize("config", [binding.CONFIG_DMA_64x64_WS, binding.CONFIG_DMA_32x32_WS])
+@pytest.mark.parametrize("integer", [False, True])
+def test_b_nk_k_rotation(config, integer):
+    # With at most 64 rows, the 64x64 and 32x32 producer tiles walk each tile's K-steps from a
+    # column-dependent start, wrapping round.  313 tiles of 64x64 (more than the CUs, so workgroups
+    # move on to tiles with another start) and K = 1000 (a partial last K-step, met anywhere in the
+    # order): bit-exact on integer inputs, within tolerance on real ones.
+    M, N, K = 48, 20032, 1000
+    if integer:
+        a, b = inputs.integer_pair(M, N, K, torch.bfloat16, seed=4848)
+    else:
+        a, b = inputs.normal_pair(M, N, K, torch.bfloat16, scale=0.05, seed=4848)
+    say(f"[B^T K rotation, config {config}, integer={integer}] GPU run")
+    got = run_nk(a, b, config)
+    want = oracle.gemm_relu(a, b, "bf16")
+    check_relu_invariants(got, "bf16")
+    if integer:
+        assert np.array_equal(got, want)
+    else:
+        assert_within_tolerance(got, want, "bf16")
+
+
 def test_b_nk_k_zero_and_empty():
     a = torch.empty((37, 0), dtype=torch.float16, device="cuda")
     bt = torch.empty((53, 0), dtype=torch.float16, device="cuda")

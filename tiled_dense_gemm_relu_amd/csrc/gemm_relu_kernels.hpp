@@ -733,7 +733,8 @@ __device__ __forceinline__ int b_swizzle(int k)
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, int GROUP_M_,
           int A_LANE_BYTES_ = 16, int B_LANE_BYTES_ = 16, bool B_KMAJOR_ = false, int PRODUCERS_ = 0,
-          bool SWIZZLE_ = true, bool XCD_REMAP_ = true, int MFMA_ = 32, bool EARLY_REFILL_ = false>
+          bool SWIZZLE_ = true, bool XCD_REMAP_ = true, int MFMA_ = 32, bool EARLY_REFILL_ = false,
+          bool K_ROTATE_ = false>
 struct DmaConfig {
     // SWIZZLE = false stores every LDS row unpermuted (the ablation of the XOR
     // swizzle; results are the same, only the bank conflicts differ).
@@ -759,6 +760,11 @@ struct DmaConfig {
     // B_KMAJOR: B is given as B^T, an (N, K) row-major array, so its LDS stage
     // has A's shape (BN rows of BK k) and its fragments are plain ds_read_b128.
     static constexpr bool B_KMAJOR = B_KMAJOR_;
+    // K_ROTATE (B stored (N, K) only): with at most 64 rows of A, each tile
+    // walks its K-steps from a start set by its column, wrapping round, instead
+    // of from 0 (see the load side of the kernel).
+    static constexpr bool K_ROTATE = K_ROTATE_;
+    static_assert(!K_ROTATE || B_KMAJOR_, "K rotation is for B stored (N, K)");
     static constexpr int A_ROW = BK * 2, B_ROW = B_KMAJOR ? BK * 2 : BN * 2;   // bytes per LDS row
     static constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * BK * 2;          // bytes per stage
     static constexpr int B_REGION = STAGES * A_STAGE;                // B stages follow the A stages
@@ -909,6 +915,18 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // 0 for B stored (K, N)), so the remaining ring steps fetch nothing
     // without a per-instruction test.
     int f_unit = 0, f_kt = 0, f_kt_end = 0, f_m0 = 0, f_n0 = 0;
+    // K rotation.  With B stored (N, K) every tile reads BK elements of each of
+    // its B^T rows per K-step; if all tiles take their K-steps in the same
+    // order, the whole chip reads the same narrow column of all N rows at once,
+    // which streams about 30% slower than spreading the tiles over K (a 128-byte
+    // column of 16384 rows of 16 KiB: 4.6 against 6.0 TB/s in a DMA-only
+    // pattern).  So, when A has at most 64 rows (it then stays in L2 whatever
+    // the order), tile column tn starts at K-step (37 tn) mod KT and wraps
+    // round; tiles of one column keep one order and still share B^T in L2.
+    // The order changes only how the fp32 sums are grouped.
+    constexpr bool KROT = Cfg::K_ROTATE && !SPLITK && KTAIL != 2;
+    const bool rotate = KROT && M <= 64;
+    int f_k0 = 0;   // with KROT: first k of the step being filled
     int32x4_t f_rsrc_a = rsrc_none, f_rsrc_bt = rsrc_none;
     const uint16_t* f_b_ptr = B;   // B stored (K, N): element (k0, f_n0) of the current step
     uint32_t f_b_bytes = 0;        // ... and the bytes its descriptor covers (a whole stage)
@@ -931,6 +949,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             f_rsrc_a = f_rsrc_bt = rsrc_none;
             f_b_bytes = 0u;
         }
+        // The tile's first K-step to fill (set on every path: a store in one
+        // branch only would keep f_k0 out of registers).  Uniform;
+        // readfirstlane keeps it in a scalar register.
+        if constexpr (KROT) f_k0 = __builtin_amdgcn_readfirstlane((rotate ? (f_n0 / BN * 37) % KT : f_kt) * BK);
     };
     fill_tile_setup();
 
@@ -942,7 +964,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
     // slot `slot`.  Steps past the end of the stream use a zero-length
     // descriptor: nothing is fetched.
     auto dma = [&](int slot, int q) {
-        const int k0 = f_kt * BK;
+        const int k0 = KROT ? f_k0 : f_kt * BK;
         if (q < QA) {
             uint32_t vo = a_voff[q], so = (uint32_t)k0 * 2u;
             if (KTAIL) {   // pieces that start past K read as zero
@@ -975,6 +997,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_relu_dma(
             fill_tile_setup();
         } else if constexpr (!Cfg::B_KMAJOR) {
             f_b_ptr += (size_t)BK * (size_t)N;
+        } else if constexpr (KROT) {
+            f_k0 += BK;
+            if (f_k0 >= KT * BK) f_k0 = 0;   // wrap round (only when rotating)
         }
     };
 
@@ -1426,12 +1451,16 @@ using DmaTile256x128WT = DmaConfig<256, 128, 32, 4, 4, 2, 4, 16, 16, true, 4>;
 // one process (a single wave with no producers: 76 us; 8 stages instead of
 // 4: no faster, so bytes in flight are not the limit).
 using DmaTile32W = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, false, 4>;
-using DmaTile32WT = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, true, 4>;
+// The B^T forms of the two producer-wave tiles that take decode-like shapes
+// (at most 64 rows) rotate each tile's K order (K_ROTATE): on 64 x 16384 x 8192
+// bf16, 48.4 against 57.9 us for the 64x64 tile; 64 x 65536 x 2048 53.5 against
+// 60.6, 16 x 32768 x 8192 91.5 against 107.6; the 32x32 tile 2-9% faster.
+using DmaTile32WT = DmaConfig<32, 32, 64, 4, 1, 1, 4, 16, 16, true, 4, true, true, 32, false, true>;
 // The 64x64x64 tile with its 4 compute waves and 4 producer waves, 4 stages:
 // on 1024^3 fp16, 6.6-7.1 us against 7.8-8.3 us for DmaTile64 (8 stages, the
 // compute waves loading), in one process with bit-identical C.
 using DmaTile64W = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, false, 4>;
-using DmaTile64WT = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, true, 4>;
+using DmaTile64WT = DmaConfig<64, 64, 64, 4, 2, 2, 4, 16, 16, true, 4, true, true, 32, false, true>;
 // The same for the 128x128x64 tile: on 2048^3 fp16, 19.3-20.1 us against
 // 21.2-21.7 us for DmaTile128, in one process with bit-identical C.
 using DmaTile128W = DmaConfig<128, 128, 64, 4, 2, 2, 4, 16, 16, false, 4>;
