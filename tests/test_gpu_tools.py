@@ -26,6 +26,21 @@ def test_layout_ablation_outputs_identical():
     assert lines[-1] == {"outputs_identical": True}
 
 
+def test_lds_read_rates():
+    """The LDS read-rate mode: each of the three fragment reads reports a rate, and a 16-byte read
+    moves more bytes per second than the 8-byte transposed read that B stored (K, N) needs."""
+    if not os.path.exists(PROGRAM):
+        pytest.fail(f"{PROGRAM} is missing: build it with python -m tiled_dense_gemm_relu_amd.build")
+    res = subprocess.run([PROGRAM, "--lds-rates"], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    lines = [json.loads(l) for l in res.stdout.splitlines() if l.startswith("{")]
+    assert sorted({l["lds_read"] for l in lines}) == ["ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16"]
+    best = {name: max(l["gb_per_s_per_cu"] for l in lines if l["lds_read"] == name) for name in
+            ("ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16")}
+    assert all(v > 0 for v in best.values())
+    assert best["ds_read_b128"] > best["ds_read_b64_tr_b16"]
+
+
 MFMA_FORM = os.path.join(os.path.dirname(PROGRAM), "mfma_form")
 
 

@@ -16,7 +16,14 @@
 //   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE ... -- ./layout_ablation --variant unswizzled
 // for its counters.
 //
+// --lds-rates instead measures how fast the LDS serves the three fragment reads
+// the kernels issue (ds_read_b128, ds_read_b64, ds_read_b64_tr_b16): 8 and 16
+// waves per CU on every CU read a 64 KiB LDS buffer at conflict-free addresses,
+// and the rate per CU follows from the bytes read and HIP events around the
+// launch.
+//
 // Usage: layout_ablation [--variant all|product|unswizzled|no_remap] [--rounds R] [--reps N] [--zero]
+//        layout_ablation --lds-rates
 // --zero: A = B = 0 instead of normal entries.  Bank conflicts and cache traffic
 // do not depend on the values, and zeros keep the shader clock at its maximum
 // (normal fp16 data drives this workload to the board's power cap), so they
@@ -84,16 +91,103 @@ float time_kernel(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int 
     return ms / reps;
 }
 
+// LDS read rate.  MODE 0: ds_read_b128 (1 KiB per wave instruction), 1:
+// ds_read_b64 (512 B), 2: ds_read_b64_tr_b16 (512 B).  Each lane reads
+// consecutive bytes, so no read has a bank conflict; per iteration a wave reads
+// 16 distinct 4 KiB slots, every address inside the 64 KiB buffer (largest:
+// 15 * 4096 + 3 * 1024 + 1023 = 65535).  The sums keep the reads live.
+constexpr int kLdsProbeBytes = 65536;
+constexpr int kLdsProbeUnroll = 16;
+
+template <int MODE, int THREADS>
+__global__ __launch_bounds__(THREADS, 1) void lds_read_rate(uint32_t* out, int iters)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t buf[kLdsProbeBytes];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    for (int i = t * 16; i < kLdsProbeBytes; i += THREADS * 16)
+        *reinterpret_cast<u32x4*>(buf + i) = u32x4{(uint32_t)i, 1u, 2u, 3u};
+    __syncthreads();
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" ::: "memory");   // each iteration reads LDS anew
+#pragma unroll
+        for (int u = 0; u < kLdsProbeUnroll; ++u) {
+            const int base = u * 4096 + (wave & 3) * 1024;
+            if constexpr (MODE == 0) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(buf + base + lane * 16);
+                acc += v.x + v.w;
+            } else if constexpr (MODE == 1) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(buf + base + lane * 8);
+                acc += v.x + v.y;
+            } else {
+                const u32x2 v = ds_read_tr16(buf + base + lane * 8);
+                acc += v.x + v.y;
+            }
+        }
+    }
+    out[blockIdx.x * THREADS + t] = acc;
+}
+
+// One workgroup of `threads` (512 or 1024: 8 or 16 waves) per CU.
+template <int MODE>
+void launch_lds_read_rate(int cus, int threads, uint32_t* out, int iters)
+{
+    if (threads == 512) lds_read_rate<MODE, 512><<<cus, 512>>>(out, iters);
+    else lds_read_rate<MODE, 1024><<<cus, 1024>>>(out, iters);
+    CHECK(hipGetLastError());
+}
+
+int lds_rates(int cus)
+{
+    constexpr int kIters = 20000;
+    uint32_t* out = nullptr;
+    CHECK(hipMalloc(&out, (size_t)cus * 1024 * sizeof(uint32_t)));
+    const char* names[3] = {"ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16"};
+    const int bytes_per_instruction[3] = {1024, 512, 512};
+    hipEvent_t t0, t1;
+    CHECK(hipEventCreate(&t0));
+    CHECK(hipEventCreate(&t1));
+    for (int round = 0; round < 2; ++round)
+        for (int threads : {512, 1024})
+            for (int mode = 0; mode < 3; ++mode) {
+                auto launch = [&]() {
+                    if (mode == 0) launch_lds_read_rate<0>(cus, threads, out, kIters);
+                    else if (mode == 1) launch_lds_read_rate<1>(cus, threads, out, kIters);
+                    else launch_lds_read_rate<2>(cus, threads, out, kIters);
+                };
+                launch();   // untimed: clocks up, code loaded
+                CHECK(hipEventRecord(t0, nullptr));
+                launch();
+                CHECK(hipEventRecord(t1, nullptr));
+                CHECK(hipEventSynchronize(t1));
+                float ms = 0.0f;
+                CHECK(hipEventElapsedTime(&ms, t0, t1));
+                const double bytes_per_cu = (double)kIters * kLdsProbeUnroll * (threads / 64) * bytes_per_instruction[mode];
+                std::printf("{\"lds_read\": \"%s\", \"waves_per_cu\": %d, \"round\": %d, \"ms\": %.3f, "
+                            "\"gb_per_s_per_cu\": %.1f}\n",
+                            names[mode], threads / 64, round, ms, bytes_per_cu / (ms * 1e6));
+                std::fflush(stdout);
+            }
+    CHECK(hipEventDestroy(t0));
+    CHECK(hipEventDestroy(t1));
+    CHECK(hipFree(out));
+    return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv)
 {
     std::string variant = "all";
     int rounds = 4, reps = 30;
-    bool zero = false;
+    bool zero = false, rates = false;
     for (int i = 1; i < argc; ++i) {
         if (!std::strcmp(argv[i], "--zero")) {
             zero = true;
+            continue;
+        }
+        if (!std::strcmp(argv[i], "--lds-rates")) {
+            rates = true;
             continue;
         }
         if (i + 1 >= argc) {
@@ -126,6 +220,7 @@ int main(int argc, char** argv)
         std::fprintf(stderr, "needs a gfx950 GPU, found %s\n", prop.gcnArchName);
         return 2;
     }
+    if (rates) return lds_rates(prop.multiProcessorCount);
     // Row-major A (M x K) and B (K x N), fp16 N(0, 0.1^2) (or zeros); the shapes
     // match the kernel's tiles exactly, so no tail instance is needed.
     uint16_t *A = nullptr, *B = nullptr;
