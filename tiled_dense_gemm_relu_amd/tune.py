@@ -5,7 +5,11 @@ the library can run for it -- the plain entry point's configurations and the
 split-K ones with 2 to 16 parts -- and records the fastest of each kind.  The
 search follows the two steps the TileLang GEMM article on zwxr.cn describes for
 its autotuner (its section 4.3): a short benchmark of every candidate as a
-prefilter, then a longer one of the few best.
+prefilter, then a longer one of the few best.  Each benchmark times back-to-back
+launches on three rotated input sets, as the bench does, so that a choice holds
+for calls that follow each other; the candidates of a stage run their timed
+regions in alternating rounds, so that the shader clock's drift reaches all of
+them alike, and each is given its median region.
 
 Output:
   * ``csrc/tuned_table.inc``: one C initialiser per shape, included by
@@ -31,7 +35,9 @@ TABLE = os.path.join(PKG, "csrc", "tuned_table.inc")
 SPLIT_CONFIGS = (4, 5, 6)          # the kernels that have split-K variants
 SPLIT_PARTS = (2, 4, 8, 16)
 PREFILTER_LAUNCHES = 5
+PREFILTER_REGIONS = 3
 FINAL_LAUNCHES = 30
+FINAL_REGIONS = 7
 BEAM = 3
 # A split-K entry is kept only if it beats the plain choice by this factor
 # (it costs a workspace).
@@ -83,7 +89,8 @@ def candidates(M, N, K, dt, layout):
     return sorted(seen)
 
 
-def time_candidate(sets, M, N, K, dt, layout, config, splits, launches, ws):
+def make_launcher(sets, M, N, K, dt, layout, config, splits, ws):
+    """One call of the candidate on input set i % len(sets), on the current stream."""
     import torch
     from . import binding
     lib = binding.load_library()
@@ -99,18 +106,36 @@ def time_candidate(sets, M, N, K, dt, layout, config, splits, launches, ws):
                                       splits, ws.data_ptr(), ws.numel(), stream.cuda_stream or None)
         if rc != 0:
             raise binding.GemmReluError(rc, binding.strerror(rc))
+    return launch
 
-    for i in range(2):
-        launch(i)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+
+def time_region(launch, launches):
+    """`launches` back-to-back launches between two events on the launch stream, as the bench
+    times a step; returns the time per launch, ms."""
+    import torch
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t0.record(stream)
     for i in range(launches):
-        ev[i][0].record(stream)
         launch(i)
-        ev[i][1].record(stream)
+    t1.record(stream)
     torch.cuda.synchronize()
-    times = sorted(s.elapsed_time(e) for s, e in ev)
-    return times[len(times) // 2]          # median, ms
+    return t0.elapsed_time(t1) / launches
+
+
+def time_alternating(launchers, launches, regions):
+    """Every candidate warmed up, then `regions` rounds in which each candidate runs one timed
+    region in turn, so that clock and power drift reach all of them alike.  Returns each
+    candidate's median region, ms per launch."""
+    for launch in launchers.values():
+        for i in range(launches):
+            launch(i)
+    times = {c: [] for c in launchers}
+    for _ in range(regions):
+        for c, launch in launchers.items():
+            times[c].append(time_region(launch, launches))
+    return {c: sorted(t)[len(t) // 2] for c, t in times.items()}
 
 
 def choose_plain(final, incumbent, margin=PLAIN_MARGIN):
@@ -130,7 +155,7 @@ def tune_shape(M, N, K, dtype, layout, log):
     dt = binding.F16 if dtype == "fp16" else binding.BF16
     tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
     sets = []
-    for seed in (1, 2):
+    for seed in (1, 2, 3):
         a, b = inputs.normal_pair(M, N, K, tdt, 0.1, seed)
         if layout == 1:
             b = b.t().contiguous()
@@ -139,16 +164,16 @@ def tune_shape(M, N, K, dtype, layout, log):
     need = max([binding.selected_splitk_config(M, N, K, dt, c, s, b_layout=layout)["workspace_bytes"]
                 for c, s in cands if s > 1] + [256])
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    pre = {c: time_candidate(sets, M, N, K, dt, layout, c[0], c[1], PREFILTER_LAUNCHES, ws) for c in cands}
-    final = {}
+    launchers = {c: make_launcher(sets, M, N, K, dt, layout, c[0], c[1], ws) for c in cands}
+    pre = time_alternating(launchers, PREFILTER_LAUNCHES, PREFILTER_REGIONS)
+    finalists = set()
     for kind in (lambda c: c[1] == 1, lambda c: c[1] > 1):
-        best = sorted((t, c) for c, t in pre.items() if kind(c))[:BEAM]
-        for _, c in best:
-            final[c] = time_candidate(sets, M, N, K, dt, layout, c[0], c[1], FINAL_LAUNCHES, ws)
-    # the current AUTO choice is always timed in the final round, so that it can be kept
+        finalists.update(c for _, c in sorted((t, c) for c, t in pre.items() if kind(c))[:BEAM])
+    # the current AUTO choice is always timed in the final rounds, so that it can be kept
     incumbent = binding.selected_config(M, N, K, dt, binding.CONFIG_AUTO, b_layout=layout)["config_id"]
-    if (incumbent, 1) in pre and (incumbent, 1) not in final:
-        final[(incumbent, 1)] = time_candidate(sets, M, N, K, dt, layout, incumbent, 1, FINAL_LAUNCHES, ws)
+    if (incumbent, 1) in pre:
+        finalists.add((incumbent, 1))
+    final = time_alternating({c: launchers[c] for c in sorted(finalists)}, FINAL_LAUNCHES, FINAL_REGIONS)
     plain = choose_plain(final, incumbent)
     split = min(((t, c) for c, t in final.items() if c[1] > 1), default=None)
     entry = {"M": M, "N": N, "K": K, "dtype": dtype, "b_layout": layout, "config": plain[1][0],
