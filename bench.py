@@ -209,7 +209,8 @@ def sample_clocks(launch, seconds, interval=0.02):
 
 
 def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, b_layout=binding.B_KN,
-                  splits=None, repeats=1, per_launch_pass=False, clock_seconds=0.0, data="normal"):
+                  splits=None, repeats=1, per_launch_pass=False, clock_seconds=0.0, data="normal",
+                  warmup_seconds=0.0):
     """Time one workload.  After `warmup` untimed launches, `repeats` timed regions of exactly
     `steps` back-to-back launches each, every region bracketed by a device synchronisation and a
     pair of GPU events on the launch stream.  Returns a dict with the median region's ms per step
@@ -218,7 +219,9 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     with clock_seconds > 0, clocks sampled while the workload runs on for that long (outside the
     timed regions).  splits: None for gemm_relu / gemm_relu_ex, else the split-K entry point with
     that many parts.  data: "normal" (the workload's N(0, 1) * scale inputs), "integer" (its
-    integer-valued variant) or "zero"."""
+    integer-valued variant) or "zero".  warmup_seconds > 0: after the `warmup` launches, further
+    untimed launches in batches of `steps` until that much wall time has passed, so that the
+    shader clock has settled at this workload's level before the first timed region."""
     sets = make_sets(w, n_sets, device, b_layout, data)
     stream = torch.cuda.current_stream(device)
     dt = binding.F16 if w.dtype == "fp16" else binding.BF16
@@ -243,9 +246,14 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
         if rc != 0:
             raise binding.GemmReluError(rc, gr.strerror(rc))
 
+    t_warm = time.perf_counter()
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize(device)
+    while time.perf_counter() - t_warm < warmup_seconds:
+        for i in range(steps):
+            launch(i)
+        torch.cuda.synchronize(device)
 
     # Timed regions: K back-to-back launches between two events, nothing else on the stream.
     # In the kernel trace they follow each other with no gap and no overlap, so a region's
@@ -468,7 +476,8 @@ def main():
                     args.b_layout == ("nk" if s_layout == binding.B_NK else "kn") and args.data == "normal"):
                 continue
             r = time_workload(sw, 50 if sw.flop < 1e12 else 20, 50, 3, device, config=s_config,
-                              b_layout=s_layout, splits=s_splits, repeats=3, per_launch_pass=True)
+                              b_layout=s_layout, splits=s_splits, repeats=3, per_launch_pass=True,
+                              warmup_seconds=0.25)
             s_ms, s_kms = r["ms_per_step"], r["ms_per_launch_between_events"]
             if s_layout == binding.B_NK:
                 name += "_b_nk"
