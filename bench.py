@@ -250,10 +250,12 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize(device)
+    warmup_launches = warmup
     while time.perf_counter() - t_warm < warmup_seconds:
         for i in range(steps):
             launch(i)
         torch.cuda.synchronize(device)
+        warmup_launches += steps
 
     # Timed regions: K back-to-back launches between two events, nothing else on the stream.
     # In the kernel trace they follow each other with no gap and no overlap, so a region's
@@ -276,7 +278,7 @@ def time_workload(w, steps, warmup, n_sets, device, config=binding.CONFIG_AUTO, 
         torch.cuda.synchronize(device)
         region_ms.append(t0.elapsed_time(t1) / steps)
     out = {"ms_per_step": sorted(region_ms)[len(region_ms) // 2], "region_ms_per_step": region_ms,
-           "clocks_first_region": before, "clocks_last_region": after}
+           "clocks_first_region": before, "clocks_last_region": after, "warmup_launches": warmup_launches}
     if per_launch_pass:
         # The same K launches once more, each between its own pair of events on the launch
         # stream.  The event records add host time to every launch and leave about 10 us
@@ -492,7 +494,8 @@ def main():
                      "TFLOP/s": round(sw.flop / (s_ms * 1e-3) / 1e12, 2),
                      "frac_mfma_peak": round(sw.flop / (s_ms * 1e-3) / 1e12 / PEAK_TFLOPS[sw.dtype], 4),
                      "GB/s": round(sw.bytes_once / (s_ms * 1e-3) / 1e9, 1),
-                     "sclk_mhz_last_region": r["clocks_last_region"]["sclk_mhz"]}
+                     "sclk_mhz_last_region": r["clocks_last_region"]["sclk_mhz"],
+                     "warmup_launches": r["warmup_launches"]}
             entry["frac_hbm_peak"] = round(entry["GB/s"] / PEAK_HBM_GBS, 4)
             secondary[name] = entry
             log(f"[bench] {name}: {entry}")
