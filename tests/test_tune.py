@@ -64,3 +64,21 @@ def test_choose_plain_keeps_the_incumbent_within_the_margin():
     assert tune.choose_plain({(9, 1): 0.05, (5, 1): 0.0499}, incumbent=3) == (0.0499, (5, 1))
     # split candidates never become the plain choice
     assert tune.choose_plain({(9, 1): 0.05, (5, 4): 0.01}, incumbent=9) == (0.05, (9, 1))
+
+
+def test_time_alternating_takes_turns_and_medians(monkeypatch):
+    """Finalists are timed region by region in turn (a drifting clock reaches each alike), each
+    warmed up first, and each gets the median of its own regions."""
+    warm, calls = [], []
+    launchers = {name: (lambda i, name=name: warm.append(name)) for name in ("a", "b")}
+    name_of = {id(f): name for name, f in launchers.items()}
+    scripted = {"a": iter([3.0, 1.0, 2.0]), "b": iter([5.0, 9.0, 4.0])}
+
+    def fake_region(launch, launches):
+        calls.append(name_of[id(launch)])
+        return next(scripted[name_of[id(launch)]])
+
+    monkeypatch.setattr(tune, "time_region", fake_region)
+    assert tune.time_alternating(launchers, launches=4, regions=3) == {"a": 2.0, "b": 5.0}
+    assert calls == ["a", "b", "a", "b", "a", "b"]
+    assert warm == ["a"] * 4 + ["b"] * 4
